@@ -1,0 +1,21 @@
+"""CPU fp64 oracle for the exact attention forward -- TEST INFRASTRUCTURE.
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
+may import this package.  The product path (the HIP library and its Python
+binding) never calls it and shares no code with it.
+
+Sources cited in this package (pages on IO-aware exact attention):
+  [P1] "FlashAttention的Triton实现：IO-aware注意力机制底层原理" (jsqmd.com)
+  [P2] "为什么Flash Attention能将注意力计算提速数倍而不损失精度：从GPU内存墙到IO感知算法的技术突围"
+       (answer.freetools.me)
+  [P3] "GPU Kernel 入门：Triton / FlashAttention" (ai.clawlihai.cn)
+
+Pinned by the CPU tests (tests/test_oracle_pins.py): the printed worked
+example of [P3] 动手, brute-force scalar evaluation, an independent library
+softmax, closed forms, invariants.  No function here is "parity unpinned".
+"""
+from .attention import (softmax_rows, online_softmax_rows, attention_head_rows,
+                        attention, attention_rows, probs_head)
+
+__all__ = ["softmax_rows", "online_softmax_rows", "attention_head_rows", "attention",
+           "attention_rows", "probs_head"]

@@ -1,0 +1,168 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one fa_fwd call over the 16K-token causal workload
+(B=1, H=32, N=16384, d=128, bf16, inputs resident in HBM).  Prints ONE JSON
+line: throughput in TFLOP/s (4*B*H*N^2*d, halved under the causal mask), the
+roofline fraction of the dominant (only) kernel against the bf16 dense MFMA
+peak, and the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS & % of MI355X bf16 MFMA peak at N=16K,d=128 (1 GPU)"
+
+# HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
+# keyed by workload; None until counters have been taken for the current kernel.
+MEASURED_TRAFFIC_BYTES = {}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_workload(w, steps, warmup):
+    import torch
+    import io_aware_exact_13_amd as fa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return total_ms, per
+
+
+def cpu_baseline(w, n_heads=4):
+    """Time the oracle on `n_heads` whole heads of the workload (every query row)."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=os.cpu_count())
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    n_heads = min(n_heads, w.B * w.H)
+    q, k, v = workloads.make_inputs(w)
+    flops = 0.0
+    t0 = time.perf_counter()
+    for i in range(n_heads):
+        b, h = divmod(i, w.H)
+        oracle.attention_head_rows(q[b, h].double().numpy(), k[b, h].double().numpy(),
+                                   v[b, h].double().numpy(), w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.N * w.N * w.d * n_heads / (2.0 if w.causal else 1.0)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_heads} of {w.B * w.H} heads of {w.name} (all {w.N} query rows each), "
+                      f"fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_exact_13_amd as fa
+    import workloads
+    from io_aware_exact_13_amd import accounting as acc
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()   # fail loudly if the HIP library is missing
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    flops = acc.attention_flops(w.B, w.H, w.N, w.d, w.causal)
+    log(f"[bench] {name}: warmup {args.warmup}, steps {args.steps}")
+    total_ms, per = time_workload(w, args.steps, args.warmup)
+    ms_step = total_ms / args.steps
+    avg_launch_ms = sum(per) / len(per)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    rows, keys, waves, blocks = fa.fa_fwd_tile(w.B, w.H, w.N, w.d, int(w.causal))
+    log(f"[bench] {ms_step:.4f} ms/step, median launch {per[len(per) // 2]:.4f} ms, "
+        f"min {per[0]:.4f} ms -> {value:.1f} TFLOP/s ({100 * value / acc.PEAK_BF16_DENSE_TFLOPS:.1f}% of peak)")
+
+    if args.all:
+        for other in workloads.WORKLOAD_ORDER:
+            ow = workloads.WORKLOADS[other]
+            tms, p = time_workload(ow, max(5, args.steps // 2), 3)
+            f = acc.attention_flops(ow.B, ow.H, ow.N, ow.d, ow.causal)
+            t = tms / max(5, args.steps // 2)
+            log(f"[bench-all] {other:32s} {t * 1e3:9.1f} us  {f / (t * 1e-3) / 1e12:7.1f} TFLOP/s "
+                f"{100 * f / (t * 1e-3) / 1e12 / acc.PEAK_BF16_DENSE_TFLOPS:5.1f}%")
+
+    traffic = MEASURED_TRAFFIC_BYTES.get(name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "seed": w.seed,
+                   "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
+                   "launch": {"rows_per_block": rows, "keys_per_tile": keys, "waves": waves,
+                              "blocks": blocks}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": acc.PEAK_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / acc.PEAK_BF16_DENSE_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

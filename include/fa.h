@@ -1,0 +1,87 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact attention forward.
+ *
+ * The operation is standard scaled dot-product attention computed without
+ * writing the N x N score or probability matrices to memory:
+ *
+ *   S = scale * Q K^T,   P = softmax(S) row-wise (optionally lower-triangular),
+ *   O = P V,             LSE_i = log(sum_j exp(S_ij))  over the visible keys j
+ *
+ * Sources (pages on IO-aware exact attention):
+ *   - "为什么Flash Attention能将注意力计算提速数倍而不损失精度", section 标准注意力机制的内存困局:
+ *     the three steps S = QK^T, P = softmax(S), O = PV.
+ *   - same page, sections 分块计算(Tiling) and 在线Softmax技巧: tiles of Q, K, V
+ *     in on-chip memory, running row maximum and exponential sum, only O and
+ *     the per-row statistics go back to HBM.
+ *   - "FlashAttention的Triton实现：IO-aware注意力机制底层原理", section Triton实现:
+ *     one program per block of query rows walking all K/V blocks (the query-
+ *     block-outer loop order), fp32 running statistics and accumulator,
+ *     probabilities rounded to the V element type before the second product.
+ *   - "GPU Kernel 入门：Triton / FlashAttention", section FlashAttention与在线softmax:
+ *     the three running statistics m, l, acc and the final acc / l.
+ * The per-row statistics are returned as one natural-log logsumexp.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  0 is success; every error is negative. */
+#define FA_OK             0
+#define FA_ERR_NULL      -1  /* a required pointer is NULL                                  */
+#define FA_ERR_SHAPE     -2  /* B, H or N <= 0, or the launch would exceed the grid limit   */
+#define FA_ERR_HEAD_DIM  -3  /* d is not 64 or 128                                          */
+#define FA_ERR_SCALE     -4  /* scale is not a finite number > 0                            */
+#define FA_ERR_ALIGN     -5  /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned  */
+#define FA_ERR_LAUNCH    -6  /* the HIP launch reported an error                            */
+#define FA_ERR_FLAG      -7  /* causal is not 0 or 1                                        */
+#define FA_ERR_ALIAS     -8  /* an output buffer overlaps an input or the other output      */
+
+/*
+ * fa_fwd -- enqueue the attention forward on `stream` and return.
+ *
+ * Arguments (all device pointers, allocated and owned by the caller):
+ *   q, k, v  bf16, [B][H][N][d], contiguous: element (b,h,n,c) sits at
+ *            ((b*H + h)*N + n)*d + c.  Read only.  16-byte aligned.
+ *   o        bf16, same layout as q; fully overwritten (round to nearest even
+ *            from the fp32 result).  16-byte aligned.
+ *   lse      fp32, [B][H][N]; fully overwritten with the natural-log
+ *            logsumexp of row n's scaled, masked scores.  4-byte aligned.
+ *   B, H, N  batch, heads, sequence length (queries and keys), each >= 1.
+ *            Any N is accepted: a ragged last tile is masked.
+ *   d        head dimension, 64 or 128.
+ *   scale    multiplier of Q K^T, finite and > 0 (typically 1/sqrt(d)).
+ *   causal   0: every query sees every key; 1: query i sees keys j <= i.
+ *   stream   HIP stream to enqueue on (0 = the null stream).
+ *
+ * Behaviour: all argument checks run on the host before any HIP call and
+ * return the codes above without touching the device.  The call allocates
+ * nothing, keeps no state between calls and is safe to call from several
+ * host threads.  It does not synchronise: faults inside the kernel surface at
+ * the caller's next synchronisation.  Outputs must not overlap the inputs or
+ * each other.  Results are bitwise reproducible run to run (no atomics).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_str(int status);
+
+/*
+ * fa_fwd_tile -- the launch shape fa_fwd uses for (N, d, causal):
+ * query rows per workgroup, keys per K/V tile, waves per workgroup and the
+ * number of workgroups for B*H heads.  Returns FA_OK or an FA_ERR_* code for
+ * arguments fa_fwd would reject (pointers are not checked here).  Host only.
+ */
+int fa_fwd_tile(int B, int H, int N, int d, int causal,
+                int* rows_per_block, int* keys_per_tile, int* waves, long long* blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

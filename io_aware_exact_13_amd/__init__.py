@@ -1,1 +1,106 @@
-"""MI355X-native fused exact attention forward (HIP, gfx950)."""
+"""MI355X-native fused exact attention forward (HIP, gfx950).
+
+Thin ctypes binding over the C ABI in include/fa.h.  Every step of the
+forward runs in the HIP library; this module only marshals arguments.  If the
+library has not been built, calls fail loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from .build import lib_path
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_HEAD_DIM = -3
+FA_ERR_SCALE = -4
+FA_ERR_ALIGN = -5
+FA_ERR_LAUNCH = -6
+FA_ERR_FLAG = -7
+FA_ERR_ALIAS = -8
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"fa_fwd failed with status {status}: {fa_status_str(status)}")
+        self.status = status
+
+
+def load_library():
+    """Load the built HIP library (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() "
+                           "or python -m io_aware_exact_13_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    lib.fa_fwd.restype = ci
+    lib.fa_status_str.argtypes = [ci]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_fwd_tile.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
+                                ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_longlong)]
+    lib.fa_fwd_tile.restype = ci
+    _lib = lib
+    return lib
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
+    """C-ABI fa_fwd with raw device addresses (ints); returns the status code."""
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale),
+                                 int(causal), stream)
+
+
+def fa_status_str(status: int) -> str:
+    return load_library().fa_status_str(int(status)).decode()
+
+
+def fa_fwd_tile(B, H, N, d, causal):
+    """(rows_per_block, keys_per_tile, waves, blocks) of the launch fa_fwd makes."""
+    r, c, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    g = ctypes.c_longlong()
+    st = load_library().fa_fwd_tile(B, H, N, d, int(causal), ctypes.byref(r), ctypes.byref(c),
+                                    ctypes.byref(w), ctypes.byref(g))
+    if st != FA_OK:
+        raise FaError(st)
+    return r.value, c.value, w.value, g.value
+
+
+def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """Attention forward on torch tensors: returns (o, lse).
+
+    q, k, v: bf16 CUDA (HIP) tensors [B, H, N, d], contiguous.  o (bf16) and
+    lse (fp32, [B, H, N]) are allocated with torch unless given.  The kernel
+    runs on `stream` (default: torch's current stream of q's device).
+    """
+    import torch
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, N, d, float(scale), int(bool(causal)), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return out, lse

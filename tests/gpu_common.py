@@ -1,0 +1,96 @@
+"""Shared helpers of the GPU parity tests: run the HIP path, compare with the oracle."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+import io_aware_exact_13_amd as fa
+import oracle
+import workloads
+
+# Required agreement between the GPU output and the fp64 oracle (bf16 inputs).
+O_MAX_ABS = 1e-2
+O_MEAN_ABS = 1e-3
+LSE_MAX_ABS = 1e-3
+
+
+def device():
+    if not torch.cuda.is_available():
+        import pytest
+        pytest.skip("no GPU")
+    if not os.path.exists(fa.lib_path()):
+        raise RuntimeError("HIP library not built")
+    return torch.device("cuda:0")
+
+
+def announce(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run_gpu(q, k, v, scale, causal, stream=None):
+    dev = device()
+    o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal, stream=stream)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def to64(t):
+    return t.double().cpu().numpy()
+
+
+def bf16_half_ulp(x):
+    """Half a bf16 unit in the last place of |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 8.0)
+
+
+def compare_full(q, k, v, scale, causal, o, lse, with_rounding=False):
+    """max|dO|, mean|dO|, max|dLSE| against the oracle.  With with_rounding, the
+    first value is max(|dO| - half a bf16 ulp of the oracle's O): the part of
+    the error not explained by O being stored in bf16."""
+    ro, rl = oracle.attention(to64(q), to64(k), to64(v), scale, causal)
+    do = np.abs(to64(o) - ro)
+    dl = np.abs(to64(lse) - rl)
+    if with_rounding:
+        return float((do - bf16_half_ulp(ro)).max()), do.mean(), dl.max(), do.max()
+    return do.max(), do.mean(), dl.max()
+
+
+def compare_rows(q, k, v, scale, causal, o, lse, picks):
+    """picks: list of (b, h, rows).  Returns max|dO|, mean|dO|, max|dLSE| over them."""
+    worst_o, worst_l, tot, cnt = 0.0, 0.0, 0.0, 0
+    q64 = k64 = v64 = None
+    for b, h, rows in picks:
+        q64 = q[b, h].double().numpy()
+        k64 = k[b, h].double().numpy()
+        v64 = v[b, h].double().numpy()
+        ro, rl = oracle.attention_head_rows(q64, k64, v64, scale, causal, rows)
+        go = o[b, h, torch.as_tensor(rows)].double().cpu().numpy()
+        gl = lse[b, h, torch.as_tensor(rows)].double().cpu().numpy()
+        d = np.abs(go - ro)
+        worst_o = max(worst_o, float(d.max()))
+        worst_l = max(worst_l, float(np.abs(gl - rl).max()))
+        tot += float(d.sum())
+        cnt += d.size
+    return worst_o, tot / cnt, worst_l
+
+
+def sample_picks(w: workloads.Workload, n_heads=3, n_rand=48, seed=0):
+    rng = np.random.default_rng(seed)
+    heads = {(0, 0), (w.B - 1, w.H - 1)}
+    while len(heads) < min(n_heads, w.B * w.H):
+        heads.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    picks = []
+    for b, h in sorted(heads):
+        rows = set(range(min(40, w.N)))
+        rows |= set(range(max(0, w.N - 40), w.N))
+        rows |= set(int(x) for x in rng.integers(0, w.N, size=n_rand))
+        # rows at query-block and key-tile boundaries
+        for edge in (63, 64, 127, 128, 129, w.N // 2 - 1, w.N // 2):
+            if 0 <= edge < w.N:
+                rows.add(edge)
+        picks.append((b, h, np.array(sorted(rows))))
+    return picks

@@ -1,0 +1,84 @@
+"""The C-ABI library: it loads, exports what include/fa.h declares, and rejects
+bad arguments on the host before any HIP call (no GPU needed, no compute)."""
+import os
+import re
+
+import pytest
+
+import io_aware_exact_13_amd as fa
+from io_aware_exact_13_amd.build import ROOT, build_library
+
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        build_library()
+    return fa.load_library()
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_fwd", "fa_fwd_tile", "fa_status_str"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEAD_DIM, fa.FA_ERR_SCALE,
+             fa.FA_ERR_ALIGN, fa.FA_ERR_LAUNCH, fa.FA_ERR_FLAG, fa.FA_ERR_ALIAS]
+    names = [fa.fa_status_str(c) for c in codes]
+    assert names[0] == "ok"
+    assert len(set(names)) == len(names)
+    assert fa.fa_status_str(-99) == "unknown status"
+
+
+# Fake, well-separated, 16-byte-aligned "device" addresses: every call below is
+# invalid in some way, so the library returns before touching HIP.
+Q, K, V, O, L = 1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40
+
+
+def call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=16, d=64, scale=0.125, causal=0):
+    return fa.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_NULL), (dict(k=0), fa.FA_ERR_NULL), (dict(v=0), fa.FA_ERR_NULL),
+    (dict(o=0), fa.FA_ERR_NULL), (dict(lse=0), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(H=-1), fa.FA_ERR_SHAPE), (dict(N=0), fa.FA_ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 20, N=1 << 20), fa.FA_ERR_SHAPE),
+    (dict(d=32), fa.FA_ERR_HEAD_DIM), (dict(d=96), fa.FA_ERR_HEAD_DIM), (dict(d=256), fa.FA_ERR_HEAD_DIM),
+    (dict(scale=float("nan")), fa.FA_ERR_SCALE), (dict(scale=float("inf")), fa.FA_ERR_SCALE),
+    (dict(scale=0.0), fa.FA_ERR_SCALE), (dict(scale=-0.1), fa.FA_ERR_SCALE),
+    (dict(causal=2), fa.FA_ERR_FLAG), (dict(causal=-1), fa.FA_ERR_FLAG),
+    (dict(q=Q + 8), fa.FA_ERR_ALIGN), (dict(o=O + 2), fa.FA_ERR_ALIGN), (dict(lse=L + 2), fa.FA_ERR_ALIGN),
+    (dict(o=Q), fa.FA_ERR_ALIAS), (dict(o=V + 16), fa.FA_ERR_ALIAS), (dict(lse=O + 64), fa.FA_ERR_ALIAS),
+    (dict(lse=K), fa.FA_ERR_ALIAS),
+])
+def test_bad_arguments_are_rejected_on_the_host(lib, kw, code):
+    assert call(**kw) == code
+
+
+def test_launch_shape_query(lib):
+    assert fa.fa_fwd_tile(1, 32, 16384, 128, 1) == (128, 64, 4, 32 * 128)
+    assert fa.fa_fwd_tile(1, 1, 1, 64, 0) == (128, 64, 4, 1)
+    assert fa.fa_fwd_tile(2, 3, 129, 64, 0)[3] == 6 * 2
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_tile(1, 1, 10, 80, 0)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import io_aware_exact_13_amd
+    monkeypatch.setattr(io_aware_exact_13_amd, "_lib", None)
+    monkeypatch.setattr(io_aware_exact_13_amd, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        io_aware_exact_13_amd.load_library()

@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy 3 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; run with --gpus 1", file=sys.stderr)
@@ -111,6 +113,14 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     fa.load_library()   # fail loudly if the HIP library is missing
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device="cuda:0")   # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied 512 MiB three times")
+        return
 
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]

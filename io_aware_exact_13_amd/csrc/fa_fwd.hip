@@ -55,62 +55,84 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kBR = 128;          // query rows per workgroup
 constexpr int kBC = 64;           // keys per K/V tile
-constexpr int kWaves = 4;         // waves per workgroup, 32 query rows each
+constexpr int kGroupWaves = 4;    // waves per ping-pong group, 32 query rows each
+constexpr int kWaves = 2 * kGroupWaves;
 constexpr int kThreads = kWaves * 64;
+constexpr int kBR = kWaves * 32;  // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;    // log2 units the reference max may lag the true max
+constexpr unsigned kNoRecord = 0x80000000u;   // buffer offset past any tile: reads return 0
 
+// LDS geometry.  Rows are padded instead of swizzled: K rows by 16 bytes, so
+// the 16 consecutive rows of an A-operand fetch start 4 banks apart; V rows
+// by 64 bytes, so the 4 rows of a transposed read start 16 banks apart.
+// Both layouts measured conflict-free on gfx950, and padding keeps every
+// per-step address a per-lane base plus an immediate.
 template <int D>
 struct Geom {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
-  static constexpr int kTileBytes = kBC * kRowBytes;       // one K or V tile
-  static constexpr int kStageBytes = 2 * kTileBytes;       // K then V
-  static constexpr int kLdsBytes = 2 * kStageBytes;        // two stages
-  static constexpr int kLoadsPerTile = kTileBytes / (kThreads * 16);
-  static_assert(kLoadsPerTile * kThreads * 16 == kTileBytes, "tile not a whole number of loads");
+  static constexpr int kRowBytes = 2 * D;                   // one K or V row in HBM
+  static constexpr int kDataChunks = kRowBytes / 16;        // 16-byte chunks with data per row
+  static constexpr int kKStride = kRowBytes + 16;
+  static constexpr int kVStride = kRowBytes + 64;
+  static constexpr int kKTile = kBC * kKStride;
+  static constexpr int kVTile = kBC * kVStride;
+  static constexpr int kKOff[2] = {0, kKTile};              // LDS byte offset of K buffer s
+  static constexpr int kVOff[2] = {2 * kKTile, 2 * kKTile + kVTile};
+  static constexpr int kLdsBytes = 2 * kKTile + 2 * kVTile;
+  static constexpr int kKSlots = kKTile / 16;               // 16-byte LDS slots per K tile
+  static constexpr int kVSlots = kVTile / 16;
+  static constexpr int kKLoads = (kKSlots + kThreads - 1) / kThreads;   // copies per thread per tile
+  static constexpr int kVLoads = (kVSlots + kThreads - 1) / kThreads;
+  // every wave-wide copy lands inside its tile
+  static_assert(kKSlots % 64 == 0 && kVSlots % 64 == 0, "tile not a whole number of wave copies");
 };
 
-// Chunk-level XOR swizzle of a tile row.  Rows r and r+k get distinct masks
-// for the 16 consecutive rows of an A-operand fetch (D=128; 8 rows for D=64),
-// and the masks of 4 aligned rows differ in bits 1..2 so that the two chunks
-// each row contributes to a transposed read land in different banks.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-  else return ((row & 3) << 1) | ((row >> 2) & 1);
-}
+// One thread's share of the HBM -> LDS copy of a tile.  Copy i of wave w fills
+// the 1 KiB of LDS at base + (kWaves i + w) KiB, lane t the 16 bytes at + 16 t,
+// so each lane fetches the global chunk that belongs in its slot.  Slots in
+// the row padding get an offset no buffer reaches (the copy writes zeros).
+template <int D, int STRIDE, int NLOADS>
+struct TileCopy {
+  unsigned voff[NLOADS];
 
-// Enqueue the HBM -> LDS copy of one K or V tile (kBC rows starting at key0).
-// global_load_lds writes lane t's 16 bytes to LDS base + 16 t, so each lane
-// fetches the global chunk that the swizzle places in its slot.  Rows past
-// the end of the sequence re-read row N-1: those keys are masked to -inf in S
-// (P = 0) and the V values they bring are finite, so they add exactly 0.
-template <int D>
-__device__ __forceinline__ void load_tile(const char* __restrict__ head, int key0, int n,
-                                          char* lds_tile, int wave, int lane) {
-  using G = Geom<D>;
+  __device__ __forceinline__ void init(int wave, int lane) {
+    constexpr int kSlotsPerRow = STRIDE / 16;
 #pragma unroll
-  for (int i = 0; i < G::kLoadsPerTile; ++i) {
-    const int slot = (i * kWaves + wave) * 1024;            // wave-uniform LDS offset
-    const int byte = slot + lane * 16;
-    const int row = byte / G::kRowBytes;
-    const int pchunk = (byte % G::kRowBytes) >> 4;
-    const int lchunk = pchunk ^ swz<D>(row);
-    const int grow = min(key0 + row, n - 1);
-    const char* src = head + (size_t)grow * G::kRowBytes + (lchunk << 4);
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds_tile + slot), 16, 0, 0);
+    for (int i = 0; i < NLOADS; ++i) {
+      const int slot = (i * kWaves + wave) * 64 + lane;
+      const int row = slot / kSlotsPerRow, chunk = slot % kSlotsPerRow;
+      const bool data = chunk < Geom<D>::kDataChunks && row < kBC;
+      voff[i] = data ? (unsigned)(row * Geom<D>::kRowBytes + chunk * 16) : kNoRecord;
+    }
   }
-}
+
+  // Copy key rows [key0, key0 + kBC) of one head into the LDS tile at `dst`.
+  // The buffer starts at row key0 and ends at row N, so rows past the end of
+  // the sequence read as zeros.
+  __device__ __forceinline__ void issue(const char* head, int key0, int n, char* dst, int wave) const {
+    // Device pass only: with the buffer-resource type in this template body,
+    // clang's host pass drops the launch stubs of some kernel instances.
+#if defined(__HIP_DEVICE_COMPILE__)
+    const char* base = head + (size_t)key0 * Geom<D>::kRowBytes;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)base, 0, (n - key0) * Geom<D>::kRowBytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < NLOADS; ++i) {
+      if ((i * kWaves + wave) * 64 < STRIDE / 16 * kBC)     // wave-uniform: skip copies past the tile
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + (i * kWaves + wave) * 1024),
+                                                 16, voff[i], 0, 0, 0);
+    }
+#endif
+  }
+};
 
 // Running state of one wave: 32 query rows, lane l owns row l % 32.
 template <int D>
@@ -120,55 +142,32 @@ struct RowState {
   float l_part;         // this lane's share of the exponential sum
 };
 
-// One K/V tile for one wave: S^T = K Q^T, mask, online softmax, O^T += V^T P^T,
-// and the copy of the next tile into the other LDS stage.  The stages are
-// passed as separate restrict pointers: nothing read here aliases the stage
-// being filled, which lets the compiler keep the asynchronous LDS copy in
-// flight across these LDS reads (the loop waits for it explicitly).
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void tile_step(const char* __restrict__ Kt, const char* __restrict__ Vt,
-                                          char* __restrict__ next_stage, bool prefetch,
-                                          const char* Kh, const char* Vh, int key0, int N,
-                                          int q0, int qrow, int wave, int lane,
-                                          const bf16x8 (&qf)[D / 16], float c_log2,
-                                          RowState<D>& st) {
+// S^T = K Q^T for one tile (fp32, unscaled).  A operand: K row 32 kb + l32,
+// columns 16 ks + 8 h .. +7; B operand: Q^T from registers.
+template <int D>
+__device__ __forceinline__ void scores(const char* Kt, int k_lane, const bf16x8 (&qf)[D / 16],
+                                       f32x16 (&s)[kBC / 32]) {
   using G = Geom<D>;
-  constexpr int kDs = D / 16;   // MFMA k-steps over the head dimension (S product)
-  constexpr int kCt = D / 32;   // 32-wide column tiles of O^T
-  constexpr int kKb = kBC / 32; // 32-key blocks of S^T per tile
-  constexpr int kKs = kBC / 16; // MFMA k-steps over keys (P V product)
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-  const int a16 = lane & 15;
-  const int cg = (lane >> 4) & 1;
-
-  if (prefetch) {
-    load_tile<D>(Kh, key0 + kBC, N, next_stage, wave, lane);
-    load_tile<D>(Vh, key0 + kBC, N, next_stage + G::kTileBytes, wave, lane);
-  }
-
-  // A wave whose rows all precede this tile's first key sees none of it.
-  if (CAUSAL && key0 > q0 + wave * 32 + 31) return;
-
-  // ---- S^T = K Q^T  (fp32, unscaled).  A operand: K row 32 kb + l32, chunk 2 ks + h.
-  const int k_swz = swz<D>(l32);                    // swz depends on row & 15 only
-  f32x16 s[kKb];
 #pragma unroll
-  for (int kb = 0; kb < kKb; ++kb) {
-    s[kb] = f32x16{};
-    const char* krow = Kt + (kb * 32 + l32) * G::kRowBytes;
+  for (int kb = 0; kb < kBC / 32; ++kb) {
+    bf16x8 a[D / 16];
 #pragma unroll
-    for (int ks = 0; ks < kDs; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (((ks * 2 + h) ^ k_swz) << 4));
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      a[ks] = *reinterpret_cast<const bf16x8*>(Kt + k_lane + kb * 32 * G::kKStride + ks * 32);
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < D / 16; ++ks)
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], s[kb], 0, 0, 0);
   }
+}
 
-  // ---- masks: keys past the end, and keys after the query under the causal mask
-  const bool tail = key0 + kBC > N;
-  const bool diag = CAUSAL && (key0 + kBC - 1 > q0 + wave * 32);
-  if (tail || diag) {
-    const int lim = CAUSAL ? min(qrow, N - 1) : (N - 1);
+// Online-softmax update for one tile: mask, row max, lazy rescale of the
+// accumulators, P = exp2(S * c - m) in bf16, row sum in fp32.
+template <int D, bool MASKED>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[kBC / 32], int key0, int lim, int h, float c_log2,
+                                             RowState<D>& st, bf16x8 (&pf)[kBC / 16]) {
+  constexpr int kKb = kBC / 32;
+  if (MASKED) {
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
@@ -177,8 +176,6 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ Kt, const cha
         if (key > lim) s[kb][r] = -INFINITY;
       }
   }
-
-  // ---- online softmax (base 2)
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < kKb; ++kb)
@@ -192,16 +189,14 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ Kt, const cha
     const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first tile
     st.l_part *= alpha;
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct)
+    for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.acc[ct][r] *= alpha;
   }
   st.m_ref = m_new;
   const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
-
   // P is summed in fp32 (the logsumexp needs the unrounded weights) and
   // rounded to bf16 for the MFMA.
-  bf16x8 pf[kKs];
   float l_even = 0.f, l_odd = 0.f;
 #pragma unroll
   for (int kb = 0; kb < kKb; ++kb)
@@ -212,30 +207,124 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ Kt, const cha
       pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
     }
   st.l_part += l_even + l_odd;
+}
 
-  // ---- O^T += V^T P^T.  k-step t covers keys 16t..16t+15 of the tile; lane
-  // half h supplies keys 16t + 4h + {0..3} (elements 0..3) and
-  // 16t + 8 + 4h + {0..3} (elements 4..7), matching the S^T layout.  The
-  // transposed read gives lane a of each 16-lane group column cbase + a of
-  // 4 consecutive rows when lane a points at row a/4, columns cbase + 4(a%4).
+// O^T += V^T P^T.  k-step t covers keys 16t..16t+15 of the tile; lane half h
+// supplies keys 16t + 4h + {0..3} (elements 0..3) and 16t + 8 + 4h + {0..3}
+// (elements 4..7), matching the S^T layout.  The transposed read gives lane a
+// of each 16-lane group column cbase + a of 4 consecutive rows when lane a
+// points at row a/4, columns cbase + 4(a%4).
+template <int D>
+__device__ __forceinline__ void accumulate_pv(const char* Vt, int v_lane, const bf16x8 (&pf)[kBC / 16],
+                                              RowState<D>& st) {
+  using G = Geom<D>;
 #pragma unroll
-  for (int t = 0; t < kKs; ++t) {
+  for (int t = 0; t < kBC / 16; ++t) {
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct) {
-      const int col = ct * 32 + cg * 16 + 4 * (a16 & 3);
-      const int chunk = col >> 3;
-      const int sub = (col & 7) * 2;
-      const int row_lo = 16 * t + 4 * h + (a16 >> 2);
-      const int row_hi = row_lo + 8;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4_t*)(Vt + row_lo * G::kRowBytes + ((chunk ^ swz<D>(row_lo)) << 4) + sub));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4_t*)(Vt + row_hi * G::kRowBytes + ((chunk ^ swz<D>(row_hi)) << 4) + sub));
+    for (int ct = 0; ct < D / 32; ++ct) {
+      const char* p = Vt + v_lane + t * 16 * G::kVStride + ct * 64;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * G::kVStride));
       const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       st.acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[t],
                                                            st.acc[ct], 0, 0, 0);
     }
   }
+}
+
+// Everything the blocks need besides the running state.
+template <int D>
+struct Ctx {
+  const char* Kh;
+  const char* Vh;
+  char* lds;
+  int N, n_tiles, lim, wave, h, k_lane, v_lane;
+  float c_log2;
+  TileCopy<D, Geom<D>::kKStride, Geom<D>::kKLoads> kcopy;
+  TileCopy<D, Geom<D>::kVStride, Geom<D>::kVLoads> vcopy;
+};
+
+// Start the copies of K_{j+2} (into K_j's buffer) and V_{j+1} (into
+// V_{j-1}'s buffer); every wave issues its share.
+template <int D>
+__device__ __forceinline__ void issue_copies(const Ctx<D>& c, int j, char* k_fill, char* v_fill) {
+  if (j + 2 < c.n_tiles) c.kcopy.issue(c.Kh, (j + 2) * kBC, c.N, k_fill, c.wave);
+  if (j + 1 < c.n_tiles) c.vcopy.issue(c.Vh, (j + 1) * kBC, c.N, v_fill, c.wave);
+}
+
+// Workgroup barrier between slots.  Not __syncthreads(): its release fence
+// would also wait for the asynchronous K/V copies, which are meant to stay in
+// flight across one slot boundary (wait_copies() waits for them explicitly).
+// Every LDS read of a block is consumed by an MFMA inside that block, so no
+// read is outstanding here; the memory clobber keeps the compiler from moving
+// LDS accesses across the barrier and the scheduling fences keep each block's
+// arithmetic inside its slot.
+__device__ __forceinline__ void slot_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// MFMA block of tile j: O += V_j P_j, then S_{j+1} = K_{j+1} Q^T.
+template <int D>
+__device__ __forceinline__ void mfma_block(const Ctx<D>& c, int j, const char* k_read, const char* v_read,
+                                           const bf16x8 (&qf)[D / 16], const bf16x8 (&pf)[kBC / 16],
+                                           f32x16 (&s)[kBC / 32], RowState<D>& st) {
+  accumulate_pv<D>(v_read, c.v_lane, pf, st);
+  if (j + 1 < c.n_tiles) scores<D>(k_read, c.k_lane, qf, s);
+}
+
+// The two groups' schedules.  Slots are separated by workgroup barriers;
+// group 0 runs MFMA blocks in even slots and VALU blocks in odd slots, group 1
+// the opposite, so on every SIMD (one wave of each group) the matrix unit
+// works on one wave's products while the other wave does its softmax.
+//   group 0:  S_0 | V(0) | M(0) | V(1) | M(1) | ... | V(n-1) | M(n-1) | -
+//   group 1:   -  | S_0  | V(0) | M(0) | V(1) | ... | M(n-2) | V(n-1) | M(n-1)
+// K_j is read in slots 2j, 2j+1 and V_j in 2j+2, 2j+3, so the copies of
+// K_{j+2} and V_{j+1} start at slot 2j+2 and are waited for at the end of
+// slot 2j+3.  A period's four buffers (K_{j+1}, V_j read; K_j's and V_{j-1}'s
+// being refilled) are distinct restrict pointers: that lets the compiler keep
+// the copies in flight across the LDS reads; the explicit waits order them.
+template <int D, bool MASKED>
+__device__ __forceinline__ void period_g0(const Ctx<D>& c, int j, const char* __restrict__ k_read,
+                                          const char* __restrict__ v_read, char* __restrict__ k_fill,
+                                          char* __restrict__ v_fill, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&s)[kBC / 32], bf16x8 (&pf)[kBC / 16], RowState<D>& st) {
+  slot_barrier();                          // slot 2j+1
+  softmax_tile<D, MASKED>(s, j * kBC, c.lim, c.h, c.c_log2, st, pf);
+  if (j > 0) wait_copies();                // copies started at slot 2j
+  slot_barrier();                          // slot 2j+2
+  issue_copies<D>(c, j, k_fill, v_fill);
+  mfma_block<D>(c, j, k_read, v_read, qf, pf, s, st);
+}
+
+template <int D, bool MASKED>
+__device__ __forceinline__ void period_g1(const Ctx<D>& c, int j, const char* __restrict__ k_read,
+                                          const char* __restrict__ v_read, char* __restrict__ k_fill,
+                                          char* __restrict__ v_fill, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&s)[kBC / 32], bf16x8 (&pf)[kBC / 16], RowState<D>& st) {
+  slot_barrier();                          // slot 2j+2
+  issue_copies<D>(c, j, k_fill, v_fill);
+  softmax_tile<D, MASKED>(s, j * kBC, c.lim, c.h, c.c_log2, st, pf);
+  slot_barrier();                          // slot 2j+3
+  mfma_block<D>(c, j, k_read, v_read, qf, pf, s, st);
+  wait_copies();
+}
+
+// Run period j of group G: buffers by the parity of j.
+template <int D, int G, bool MASKED>
+__device__ __forceinline__ void period(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
+                                       f32x16 (&s)[kBC / 32], bf16x8 (&pf)[kBC / 16], RowState<D>& st) {
+  using Gm = Geom<D>;
+  const int par = j & 1;
+  char* k_same = c.lds + par * Gm::kKTile;                        // K_j's buffer
+  char* k_other = c.lds + (par ^ 1) * Gm::kKTile;                 // K_{j+1}
+  char* v_same = c.lds + 2 * Gm::kKTile + par * Gm::kVTile;       // V_j
+  char* v_other = c.lds + 2 * Gm::kKTile + (par ^ 1) * Gm::kVTile;  // V_{j-1}, refilled with V_{j+1}
+  if (G == 0) period_g0<D, MASKED>(c, j, k_other, v_same, k_same, v_other, qf, s, pf, st);
+  else        period_g1<D, MASKED>(c, j, k_other, v_same, k_same, v_other, qf, s, pf, st);
 }
 
 template <int D, bool CAUSAL>
@@ -249,40 +338,57 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   __shared__ __attribute__((aligned(1024))) char lds[G::kLdsBytes];
 
+  Ctx<D> c;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5;      // which half of the 64 lanes
-  const int l32 = lane & 31;    // this lane's query row within the wave
+  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.h = lane >> 5;                  // which half of the 64 lanes
+  const int l32 = lane & 31;        // this lane's query row within the wave
+  const int group = c.wave / kGroupWaves;
 
   // ---- workgroup -> (head, query block)
   const int wg = blockIdx.x;
   const int bh = wg % BH;
   const int qb = CAUSAL ? (n_qblocks - 1 - wg / BH) : (wg / BH);
   const int q0 = qb * kBR;
-  const int qrow = q0 + wave * 32 + l32;               // this lane's query
+  const int qrow = q0 + c.wave * 32 + l32;   // this lane's query
+  c.N = N;
+  c.lim = CAUSAL ? min(qrow, N - 1) : N - 1;   // last key this lane may see
+  c.c_log2 = c_log2;
+  c.lds = lds;
 
   const size_t head_off = (size_t)bh * (size_t)N * D;
-  const char* Kh = reinterpret_cast<const char*>(K + head_off);
-  const char* Vh = reinterpret_cast<const char*>(V + head_off);
+  c.Kh = reinterpret_cast<const char*>(K + head_off);
+  c.Vh = reinterpret_cast<const char*>(V + head_off);
 
-  // ---- key range
-  int kv_end = N;
-  if (CAUSAL) kv_end = min(N, q0 + kBR);
-  const int n_tiles = (kv_end + kBC - 1) / kBC;
+  // ---- key tiles: every wave walks the workgroup's n_tiles (under the causal
+  // mask, tiles wholly past a wave's rows are masked out by its softmax).
+  const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  c.n_tiles = (kv_end + kBC - 1) / kBC;
+  // tiles from j_mask on hold keys past the end or past some query of the block
+  int j_mask = (N - 1) / kBC;                           // the tile holding key N-1
+  if (CAUSAL) j_mask = min(j_mask, q0 / kBC);           // first tile with a key > q0
+  j_mask = min(j_mask, c.n_tiles);
 
-  // ---- start the first K/V tile while Q is fetched
-  load_tile<D>(Kh, 0, N, lds, wave, lane);
-  load_tile<D>(Vh, 0, N, lds + G::kTileBytes, wave, lane);
+  // ---- per-lane offsets
+  c.k_lane = l32 * G::kKStride + c.h * 16;
+  c.v_lane = (4 * c.h + ((lane & 15) >> 2)) * G::kVStride + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+  c.kcopy.init(c.wave, lane);
+  c.vcopy.init(c.wave, lane);
 
-  // ---- Q^T operand: lane holds Q[qrow][16*ks + 8*h .. +7] for each k-step
+  // ---- prologue: K_0, V_0, K_1 in flight while Q is fetched
+  c.kcopy.issue(c.Kh, 0, N, lds + G::kKOff[0], c.wave);
+  c.vcopy.issue(c.Vh, 0, N, lds + G::kVOff[0], c.wave);
+  if (c.n_tiles > 1) c.kcopy.issue(c.Kh, kBC, N, lds + G::kKOff[1], c.wave);
+
+  // Q^T operand: lane holds Q[qrow][16*ks + 8*h .. +7] for each k-step
   bf16x8 qf[kDs];
   {
     const bool ok = qrow < N;
     const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + head_off + (size_t)(ok ? qrow : 0) * D);
 #pragma unroll
     for (int ks = 0; ks < kDs; ++ks) {
-      bf16x8 x = src[ks * 2 + h];
+      bf16x8 x = src[ks * 2 + c.h];
       if (!ok) x = bf16x8{};
       qf[ks] = x;
     }
@@ -293,18 +399,23 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int ct = 0; ct < kCt; ++ct) st.acc[ct] = f32x16{};
   st.m_ref = -INFINITY;
   st.l_part = 0.f;
+  f32x16 s[kBC / 32];
+  bf16x8 pf[kBC / 16];
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
-    char* cur = lds + stage * G::kStageBytes;
-    char* nxt = lds + (stage ^ 1) * G::kStageBytes;
-    // Tile j has landed (this thread's copies); after the barrier everyone's
-    // copies are visible and everyone has finished tile j-1, whose stage the
-    // next copy overwrites.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    tile_step<D, CAUSAL>(cur, cur + G::kTileBytes, nxt, j + 1 < n_tiles, Kh, Vh, j * kBC, N,
-                         q0, qrow, wave, lane, qf, c_log2, st);
+  wait_copies();
+  slot_barrier();                                 // slot 0
+  if (group == 0) {
+    scores<D>(lds + G::kKOff[0], c.k_lane, qf, s);
+    int j = 0;
+    for (; j < j_mask; ++j) period<D, 0, false>(c, j, qf, s, pf, st);
+    for (; j < c.n_tiles; ++j) period<D, 0, true>(c, j, qf, s, pf, st);
+    slot_barrier();                               // slot 2n+1: idle
+  } else {
+    slot_barrier();                               // slot 1
+    scores<D>(lds + G::kKOff[0], c.k_lane, qf, s);
+    int j = 0;
+    for (; j < j_mask; ++j) period<D, 1, false>(c, j, qf, s, pf, st);
+    for (; j < c.n_tiles; ++j) period<D, 1, true>(c, j, qf, s, pf, st);
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m_ref + log2 l) * ln 2
@@ -316,7 +427,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int c0 = ct * 32 + r4 * 8 + h * 4;
+        const int c0 = ct * 32 + r4 * 8 + c.h * 4;
         const __bf16 b0 = (__bf16)(st.acc[ct][r4 * 4 + 0] * inv);
         const __bf16 b1 = (__bf16)(st.acc[ct][r4 * 4 + 1] * inv);
         const __bf16 b2 = (__bf16)(st.acc[ct][r4 * 4 + 2] * inv);
@@ -326,7 +437,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         w[1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
         *reinterpret_cast<u32x2*>(orow + c0) = w;
       }
-    if (h == 0) LSE[(size_t)bh * N + qrow] = (st.m_ref + log2f(l_tot)) * kLn2;
+    if (c.h == 0) LSE[(size_t)bh * N + qrow] = (st.m_ref + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -361,6 +472,8 @@ static int check_shape(int B, int H, int N, int d, int causal, long long* blocks
   const long long g = bh * nqb;
   // grid size in work-items must fit 32 bits; heads must index in int
   if (bh > 0x7fffffffLL || g * kThreads > 0xffffffffLL) return FA_ERR_SHAPE;
+  // one head's K or V must stay below 2 GiB (buffer offsets are 32-bit)
+  if ((long long)N * d * 2 >= 0x80000000LL) return FA_ERR_SHAPE;
   *blocks = g;
   return FA_OK;
 }

@@ -69,9 +69,12 @@ def test_bad_arguments_are_rejected_on_the_host(lib, kw, code):
 
 
 def test_launch_shape_query(lib):
-    assert fa.fa_fwd_tile(1, 32, 16384, 128, 1) == (128, 64, 4, 32 * 128)
-    assert fa.fa_fwd_tile(1, 1, 1, 64, 0) == (128, 64, 4, 1)
-    assert fa.fa_fwd_tile(2, 3, 129, 64, 0)[3] == 6 * 2
+    rows, keys, waves, blocks = fa.fa_fwd_tile(1, 32, 16384, 128, 1)
+    assert rows == 32 * waves and keys in (32, 64, 128)
+    assert blocks == 32 * (16384 // rows)
+    assert fa.fa_fwd_tile(1, 1, 1, 64, 0)[3] == 1
+    r = fa.fa_fwd_tile(2, 3, 129, 64, 0)[0]
+    assert fa.fa_fwd_tile(2, 3, 129, 64, 0)[3] == 6 * (-(-129 // r))
     with pytest.raises(fa.FaError):
         fa.fa_fwd_tile(1, 1, 10, 80, 0)
 

@@ -189,9 +189,11 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[kBC / 32], int key0, in
     const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first tile
     st.l_part *= alpha;
 #pragma unroll
-    for (int ct = 0; ct < D / 32; ++ct)
+    for (int ct = 0; ct < D / 32; ++ct) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.acc[ct][r] *= alpha;
+      asm volatile("" : "+v"(st.acc[ct]));
+    }
   }
   st.m_ref = m_new;
   const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
@@ -207,6 +209,12 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[kBC / 32], int key0, in
       pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
     }
   st.l_part += l_even + l_odd;
+  // Materialise P and the statistics here: without these empty asm uses the
+  // compiler sinks the exponentials next to the MFMAs that consume them,
+  // i.e. into the other slot, which defeats the ping-pong.
+#pragma unroll
+  for (int t = 0; t < kBC / 16; ++t) asm volatile("" : "+v"(pf[t]));
+  asm volatile("" : "+v"(st.l_part), "+v"(st.m_ref));
 }
 
 // O^T += V^T P^T.  k-step t covers keys 16t..16t+15 of the tile; lane half h
@@ -267,13 +275,70 @@ __device__ __forceinline__ void slot_barrier() {
 
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// MFMA block of tile j: O += V_j P_j, then S_{j+1} = K_{j+1} Q^T.
+// MFMA block of tile j: O += V_j P_j (16 MFMAs at d=128), then
+// S_{j+1} = K_{j+1} Q^T (16 MFMAs), as one software-pipelined stream: the LDS
+// operands of step i + kAhead are requested before the MFMA of step i, so each
+// MFMA finds its operand already in registers.  Only one wave per SIMD is in
+// its MFMA block at a time, so the block has to hide its own LDS latency.
+// Consecutive MFMAs write different accumulators.  S_{j+1} is computed even
+// after the last tile (from whatever the buffer holds; the result is unused)
+// to keep the block branch-free.
 template <int D>
-__device__ __forceinline__ void mfma_block(const Ctx<D>& c, int j, const char* k_read, const char* v_read,
+__device__ __forceinline__ void mfma_block(const Ctx<D>& c, const char* k_read, const char* v_read,
                                            const bf16x8 (&qf)[D / 16], const bf16x8 (&pf)[kBC / 16],
                                            f32x16 (&s)[kBC / 32], RowState<D>& st) {
-  accumulate_pv<D>(v_read, c.v_lane, pf, st);
-  if (j + 1 < c.n_tiles) scores<D>(k_read, c.k_lane, qf, s);
+  using G = Geom<D>;
+  constexpr int kCt = D / 32, kKs = kBC / 16, kKb = kBC / 32, kDs = D / 16;
+  constexpr int kPV = kKs * kCt;        // P V steps: (t, ct), ct fastest
+  constexpr int kS = kDs * kKb;         // S steps: (ks, kb), kb fastest
+  constexpr int kSteps = kPV + kS;
+  constexpr int kAhead = 8;
+  bf16x8 opnd[kSteps];
+  auto fetch = [&](int i) {
+    if (i < kPV) {
+      const int t = i / kCt, ct = i % kCt;
+      const char* p = v_read + c.v_lane + t * 16 * G::kVStride + ct * 64;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * G::kVStride));
+      opnd[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      const int ks = (i - kPV) / kKb, kb = (i - kPV) % kKb;
+      opnd[i] = *reinterpret_cast<const bf16x8*>(k_read + c.k_lane + kb * 32 * G::kKStride + ks * 32);
+    }
+  };
+  auto mfma = [&](int i) {
+    if (i < kPV) {
+      const int t = i / kCt, ct = i % kCt;
+      st.acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i], pf[t], st.acc[ct], 0, 0, 0);
+    } else {
+      const int ks = (i - kPV) / kKb, kb = (i - kPV) % kKb;
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i], qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
+    }
+  };
+  static_assert(kPV >= kAhead && kS >= kAhead, "pipeline deeper than a phase");
+  // Scheduling groups (mask 0x100: LDS reads, 0x008: MFMA) pin the order.
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) fetch(i);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < kPV - kAhead; ++i) {          // P V steps, prefetching P V operands
+    fetch(i + kAhead);
+    mfma(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+#pragma unroll
+  for (int i = kPV - kAhead; i < kSteps - kAhead; ++i) {   // prefetching S operands
+    fetch(i + kAhead);
+    mfma(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+#pragma unroll
+  for (int i = kSteps - kAhead; i < kSteps; ++i) {
+    mfma(i);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
 }
 
 // The two groups' schedules.  Slots are separated by workgroup barriers;
@@ -297,7 +362,7 @@ __device__ __forceinline__ void period_g0(const Ctx<D>& c, int j, const char* __
   if (j > 0) wait_copies();                // copies started at slot 2j
   slot_barrier();                          // slot 2j+2
   issue_copies<D>(c, j, k_fill, v_fill);
-  mfma_block<D>(c, j, k_read, v_read, qf, pf, s, st);
+  mfma_block<D>(c, k_read, v_read, qf, pf, s, st);
 }
 
 template <int D, bool MASKED>
@@ -309,7 +374,7 @@ __device__ __forceinline__ void period_g1(const Ctx<D>& c, int j, const char* __
   issue_copies<D>(c, j, k_fill, v_fill);
   softmax_tile<D, MASKED>(s, j * kBC, c.lim, c.h, c.c_log2, st, pf);
   slot_barrier();                          // slot 2j+3
-  mfma_block<D>(c, j, k_read, v_read, qf, pf, s, st);
+  mfma_block<D>(c, k_read, v_read, qf, pf, s, st);
   wait_copies();
 }
 

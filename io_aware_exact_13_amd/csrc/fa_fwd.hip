@@ -62,8 +62,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int kBC = 64;           // keys per K/V tile
-constexpr int kGroupWaves = 4;    // waves per ping-pong group, 32 query rows each
-constexpr int kWaves = 2 * kGroupWaves;
+constexpr int kWaves = 8;         // waves per workgroup, 32 query rows each
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * 32;  // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
@@ -71,68 +70,79 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;    // log2 units the reference max may lag the true max
 constexpr unsigned kNoRecord = 0x80000000u;   // buffer offset past any tile: reads return 0
 
-// LDS geometry.  Rows are padded instead of swizzled: K rows by 16 bytes, so
-// the 16 consecutive rows of an A-operand fetch start 4 banks apart; V rows
-// by 64 bytes, so the 4 rows of a transposed read start 16 banks apart.
-// Both layouts measured conflict-free on gfx950, and padding keeps every
-// per-step address a per-lane base plus an immediate.
+// LDS geometry: unpadded rows with XOR-swizzled 16-byte chunks, so a tile is
+// exactly 16 KiB (d=128) and every wave copies the same number of 1 KiB
+// pieces of it.  K: chunk c of row r sits at chunk c ^ fk(r); the 16
+// consecutive rows of an A-operand fetch then cover all 64 banks.  V: the
+// mask moves whole 64-byte column groups (fv(r) touches only the group bits),
+// so the 4 rows of one transposed read land in 4 different bank groups.  Both
+// masks depend on the row modulo 16, which a 32-row or 16-row step does not
+// change.
 template <int D>
 struct Geom {
-  static constexpr int kRowBytes = 2 * D;                   // one K or V row in HBM
-  static constexpr int kDataChunks = kRowBytes / 16;        // 16-byte chunks with data per row
-  static constexpr int kKStride = kRowBytes + 16;
-  static constexpr int kVStride = kRowBytes + 64;
-  static constexpr int kKTile = kBC * kKStride;
-  static constexpr int kVTile = kBC * kVStride;
-  static constexpr int kKOff[2] = {0, kKTile};              // LDS byte offset of K buffer s
-  static constexpr int kVOff[2] = {2 * kKTile, 2 * kKTile + kVTile};
-  static constexpr int kLdsBytes = 2 * kKTile + 2 * kVTile;
-  static constexpr int kKSlots = kKTile / 16;               // 16-byte LDS slots per K tile
-  static constexpr int kVSlots = kVTile / 16;
-  static constexpr int kKLoads = (kKSlots + kThreads - 1) / kThreads;   // copies per thread per tile
-  static constexpr int kVLoads = (kVSlots + kThreads - 1) / kThreads;
-  // every wave-wide copy lands inside its tile
-  static_assert(kKSlots % 64 == 0 && kVSlots % 64 == 0, "tile not a whole number of wave copies");
+  static constexpr int kRowBytes = 2 * D;                   // one K or V row
+  static constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
+  static constexpr int kTile = kBC * kRowBytes;             // one K or V tile
+  static constexpr int kKOff0 = 0, kKOff1 = kTile;          // two K buffers, two V buffers
+  static constexpr int kVOff0 = 2 * kTile, kVOff1 = 3 * kTile;
+  static constexpr int kLdsBytes = 4 * kTile;
+  static constexpr int kLoads = kTile / (kThreads * 16);    // 1 KiB copies per wave per tile
+  static_assert(kLoads * kThreads * 16 == kTile, "tile not a whole number of wave copies");
+  __host__ __device__ static constexpr int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  __host__ __device__ static constexpr int fv(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 };
 
-// One thread's share of the HBM -> LDS copy of a tile.  Copy i of wave w fills
-// the 1 KiB of LDS at base + (kWaves i + w) KiB, lane t the 16 bytes at + 16 t,
-// so each lane fetches the global chunk that belongs in its slot.  Slots in
-// the row padding get an offset no buffer reaches (the copy writes zeros).
-template <int D, int STRIDE, int NLOADS>
+// One thread's share of the HBM -> LDS copy of a tile (buffer_load ... lds).
+// Copy i of wave w fills the 1 KiB of LDS at base + (kWaves i + w) KiB, lane t
+// the 16 bytes at + 16 t, so each lane fetches the global chunk that the
+// swizzle puts in its slot.  The swizzle of a slot's row does not depend on
+// i, so copy i reads at the lane's offset plus i * kWaves KiB.
+template <int D, bool IS_V>
 struct TileCopy {
-  unsigned voff[NLOADS];
+  unsigned voff;
 
   __device__ __forceinline__ void init(int wave, int lane) {
-    constexpr int kSlotsPerRow = STRIDE / 16;
-#pragma unroll
-    for (int i = 0; i < NLOADS; ++i) {
-      const int slot = (i * kWaves + wave) * 64 + lane;
-      const int row = slot / kSlotsPerRow, chunk = slot % kSlotsPerRow;
-      const bool data = chunk < Geom<D>::kDataChunks && row < kBC;
-      voff[i] = data ? (unsigned)(row * Geom<D>::kRowBytes + chunk * 16) : kNoRecord;
-    }
+    using G = Geom<D>;
+    const int slot = wave * 64 + lane;
+    const int row = slot / G::kChunks, pchunk = slot % G::kChunks;
+    const int lchunk = pchunk ^ (IS_V ? G::fv(row) : G::fk(row));
+    voff = (unsigned)(row * G::kRowBytes + lchunk * 16);
   }
 
   // Copy key rows [key0, key0 + kBC) of one head into the LDS tile at `dst`.
-  // The buffer starts at row key0 and ends at row N, so rows past the end of
-  // the sequence read as zeros.
-  __device__ __forceinline__ void issue(const char* head, int key0, int n, char* dst, int wave) const {
+  // The buffer runs from row key0 to row N: rows past the end read as zeros,
+  // and a tile wholly past the end copies nothing but zeros (no branch).
+  __device__ __forceinline__ void issue(const char* head, int key0, int n, char* dst, int wave, int i) const {
+    using G = Geom<D>;
     // Device pass only: with the buffer-resource type in this template body,
     // clang's host pass drops the launch stubs of some kernel instances.
 #if defined(__HIP_DEVICE_COMPILE__)
-    const char* base = head + (size_t)key0 * Geom<D>::kRowBytes;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)base, 0, (n - key0) * Geom<D>::kRowBytes, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < NLOADS; ++i) {
-      if ((i * kWaves + wave) * 64 < STRIDE / 16 * kBC)     // wave-uniform: skip copies past the tile
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + (i * kWaves + wave) * 1024),
-                                                 16, voff[i], 0, 0, 0);
-    }
+    const int rows = max(n - key0, 0);
+    const char* base = head + (size_t)min(key0, n) * G::kRowBytes;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, rows * G::kRowBytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + (i * kWaves + wave) * 1024), 16,
+                                             voff + i * kWaves * 1024, 0, 0, 0);
 #endif
   }
 };
+
+// Combine a per-lane value with the lane 32 apart using the gfx950
+// cross-half swap (a VALU op; a shuffle would go through the LDS crossbar).
+// After the swap of x with itself, the two results hold, in every lane, the
+// values of lanes l % 32 and l % 32 + 32 -- in either order, which max and sum
+// do not care about.
+__device__ __forceinline__ float max_halves(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
 
 // Running state of one wave: 32 query rows, lane l owns row l % 32.
 template <int D>
@@ -142,10 +152,11 @@ struct RowState {
   float l_part;         // this lane's share of the exponential sum
 };
 
-// S^T = K Q^T for one tile (fp32, unscaled).  A operand: K row 32 kb + l32,
-// columns 16 ks + 8 h .. +7; B operand: Q^T from registers.
+// S^T = K Q^T for one tile (fp32, unscaled), not overlapped with anything
+// (used once, for S_0).  A operand: K row 32 kb + l32, columns 16 ks + 8 h
+// .. +7; B operand: Q^T from registers.
 template <int D>
-__device__ __forceinline__ void scores(const char* Kt, int k_lane, const bf16x8 (&qf)[D / 16],
+__device__ __forceinline__ void scores(const char* Kt, const int (&k_off)[D / 16], const bf16x8 (&qf)[D / 16],
                                        f32x16 (&s)[kBC / 32]) {
   using G = Geom<D>;
 #pragma unroll
@@ -153,7 +164,7 @@ __device__ __forceinline__ void scores(const char* Kt, int k_lane, const bf16x8 
     bf16x8 a[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      a[ks] = *reinterpret_cast<const bf16x8*>(Kt + k_lane + kb * 32 * G::kKStride + ks * 32);
+      a[ks] = *reinterpret_cast<const bf16x8*>(Kt + k_off[ks] + kb * 32 * G::kRowBytes);
     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
     for (int ks = 1; ks < D / 16; ++ks)
@@ -161,11 +172,27 @@ __device__ __forceinline__ void scores(const char* Kt, int k_lane, const bf16x8 
   }
 }
 
-// Online-softmax update for one tile: mask, row max, lazy rescale of the
-// accumulators, P = exp2(S * c - m) in bf16, row sum in fp32.
+// Transposed read of the V^T operand for P V k-step t, column tile ct: lane
+// a of each 16-lane group points at row a/4 of a 4-row group, columns
+// cbase + 4(a%4), and receives column cbase + a of the 4 rows; the two
+// reads cover keys 16t + 4h + {0..3} and 16t + 8 + 4h + {0..3}, the keys the
+// lane's half holds in the S^T accumulator layout.
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(const char* Vt, int v_off_ct, int t) {
+  using G = Geom<D>;
+  const char* p = Vt + v_off_ct + t * 16 * G::kRowBytes;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * G::kRowBytes));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Online-softmax update for one tile: mask, row max, reference-max update,
+// P = exp2(S * c - m) in bf16, row sum in fp32.  Returns alpha, the factor
+// the accumulators must be multiplied by (1 unless the reference moved), and
+// sets *rescale when some lane of the wave needs it.
 template <int D, bool MASKED>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[kBC / 32], int key0, int lim, int h, float c_log2,
-                                             RowState<D>& st, bf16x8 (&pf)[kBC / 16]) {
+__device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, int lim, int h, float c_log2,
+                                              RowState<D>& st, bf16x8 (&pf)[kBC / 16], bool* rescale) {
   constexpr int kKb = kBC / 32;
   if (MASKED) {
 #pragma unroll
@@ -176,220 +203,162 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[kBC / 32], int key0, in
         if (key > lim) s[kb][r] = -INFINITY;
       }
   }
-  float mx = -INFINITY;
+  // row max: a three-way tree over this lane's 16 kKb scores (v_max3),
+  // then the other half's
+  float part[16 * kKb];
 #pragma unroll
   for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_tile = mx * c_log2;
+    for (int r = 0; r < 16; ++r) part[kb * 16 + r] = s[kb][r];
+  int n = 16 * kKb;
+#pragma unroll
+  for (int round = 0; round < 6; ++round) {
+    if (n <= 1) break;
+    const int m = (n + 2) / 3;
+#pragma unroll
+    for (int r = 0; r < m; ++r) {
+      const float a = part[3 * r];
+      const float b = 3 * r + 1 < n ? part[3 * r + 1] : a;
+      const float c = 3 * r + 2 < n ? part[3 * r + 2] : a;
+      part[r] = fmaxf(a, fmaxf(b, c));
+    }
+    n = m;
+  }
+  const float m_tile = max_halves(part[0]) * c_log2;
   const bool grow = m_tile > st.m_ref + kSlack;
   const float m_new = grow ? m_tile : st.m_ref;
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-    const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first tile
-    st.l_part *= alpha;
-#pragma unroll
-    for (int ct = 0; ct < D / 32; ++ct) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[ct][r] *= alpha;
-      asm volatile("" : "+v"(st.acc[ct]));
-    }
-  }
+  *rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
+  const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first tile
   st.m_ref = m_new;
   const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
   // P is summed in fp32 (the logsumexp needs the unrounded weights) and
   // rounded to bf16 for the MFMA.
-  float l_even = 0.f, l_odd = 0.f;
+  float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, neg_m));
-      if (r & 1) l_odd += p; else l_even += p;
+      l4[r & 3] += p;
       pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
     }
-  st.l_part += l_even + l_odd;
+  st.l_part = st.l_part * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
   // Materialise P and the statistics here: without these empty asm uses the
-  // compiler sinks the exponentials next to the MFMAs that consume them,
-  // i.e. into the other slot, which defeats the ping-pong.
+  // compiler sinks the exponentials into the next step, next to the MFMAs
+  // that consume them, where they would no longer overlap this step's MFMAs.
 #pragma unroll
   for (int t = 0; t < kBC / 16; ++t) asm volatile("" : "+v"(pf[t]));
   asm volatile("" : "+v"(st.l_part), "+v"(st.m_ref));
+  return alpha;
 }
 
-// O^T += V^T P^T.  k-step t covers keys 16t..16t+15 of the tile; lane half h
-// supplies keys 16t + 4h + {0..3} (elements 0..3) and 16t + 8 + 4h + {0..3}
-// (elements 4..7), matching the S^T layout.  The transposed read gives lane a
-// of each 16-lane group column cbase + a of 4 consecutive rows when lane a
-// points at row a/4, columns cbase + 4(a%4).
-template <int D>
-__device__ __forceinline__ void accumulate_pv(const char* Vt, int v_lane, const bf16x8 (&pf)[kBC / 16],
-                                              RowState<D>& st) {
-  using G = Geom<D>;
-#pragma unroll
-  for (int t = 0; t < kBC / 16; ++t) {
-#pragma unroll
-    for (int ct = 0; ct < D / 32; ++ct) {
-      const char* p = Vt + v_lane + t * 16 * G::kVStride + ct * 64;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * G::kVStride));
-      const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      st.acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[t],
-                                                           st.acc[ct], 0, 0, 0);
-    }
-  }
-}
-
-// Everything the blocks need besides the running state.
+// Everything a pipeline step needs besides the running state.
 template <int D>
 struct Ctx {
   const char* Kh;
   const char* Vh;
   char* lds;
-  int N, n_tiles, lim, wave, h, k_lane, v_lane;
+  int N, n_tiles, lim, wave, h;
   float c_log2;
-  TileCopy<D, Geom<D>::kKStride, Geom<D>::kKLoads> kcopy;
-  TileCopy<D, Geom<D>::kVStride, Geom<D>::kVLoads> vcopy;
+  int k_off[D / 16];    // lane's LDS offset of its K operand for k-step ks (32-row block 0)
+  int v_off[D / 32];    // lane's LDS offset of its first transposed V read for column tile ct
+  TileCopy<D, false> kcopy;
+  TileCopy<D, true> vcopy;
 };
 
-// Start the copies of K_{j+2} (into K_j's buffer) and V_{j+1} (into
-// V_{j-1}'s buffer); every wave issues its share.
-template <int D>
-__device__ __forceinline__ void issue_copies(const Ctx<D>& c, int j, char* k_fill, char* v_fill) {
-  if (j + 2 < c.n_tiles) c.kcopy.issue(c.Kh, (j + 2) * kBC, c.N, k_fill, c.wave);
-  if (j + 1 < c.n_tiles) c.vcopy.issue(c.Vh, (j + 1) * kBC, c.N, v_fill, c.wave);
-}
-
-// Workgroup barrier between slots.  Not __syncthreads(): its release fence
-// would also wait for the asynchronous K/V copies, which are meant to stay in
-// flight across one slot boundary (wait_copies() waits for them explicitly).
-// Every LDS read of a block is consumed by an MFMA inside that block, so no
-// read is outstanding here; the memory clobber keeps the compiler from moving
-// LDS accesses across the barrier and the scheduling fences keep each block's
-// arithmetic inside its slot.
-__device__ __forceinline__ void slot_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// MFMA block of tile j: O += V_j P_j (16 MFMAs at d=128), then
-// S_{j+1} = K_{j+1} Q^T (16 MFMAs), as one software-pipelined stream: the LDS
-// operands of step i + kAhead are requested before the MFMA of step i, so each
-// MFMA finds its operand already in registers.  Only one wave per SIMD is in
-// its MFMA block at a time, so the block has to hide its own LDS latency.
-// Consecutive MFMAs write different accumulators.  S_{j+1} is computed even
-// after the last tile (from whatever the buffer holds; the result is unused)
-// to keep the block branch-free.
-template <int D>
-__device__ __forceinline__ void mfma_block(const Ctx<D>& c, const char* k_read, const char* v_read,
-                                           const bf16x8 (&qf)[D / 16], const bf16x8 (&pf)[kBC / 16],
-                                           f32x16 (&s)[kBC / 32], RowState<D>& st) {
+// One pipeline step, iteration j on LDS parity PAR = j & 1.  In flight on
+// entry: S_j (fp32, in s_in) and P_{j-1} (bf16, in p_in); K_{j+1} and V_{j-1}
+// have landed in LDS (K in buffer PAR^1, V in buffer PAR^1).  The step
+//   - starts the copies of K_{j+2} (into K_j's buffer PAR) and V_j (into V_{j-2}'s
+//     buffer PAR), read in the next two steps;
+//   - runs, as one interleaved instruction stream, the MFMAs of
+//     S_{j+1} = K_{j+1} Q^T and of O += V_{j-1} P_{j-1} together with the
+//     softmax of tile j (S_j -> P_j): the wave's own VALU work issues in the
+//     shadow of its MFMAs;
+//   - if the reference maximum moved, multiplies O by alpha_j after the
+//     O += V_{j-1} P_{j-1} products (O must not yet hold tile j).
+// The LDS buffers read and the ones being filled are distinct restrict
+// pointers: the compiler then keeps the copies in flight across the reads
+// (the next step's explicit wait orders them).
+template <int D, bool MASKED>
+__device__ __forceinline__ void step(const char* __restrict__ k_read, const char* __restrict__ v_read,
+                                     char* __restrict__ k_fill, char* __restrict__ v_fill, const Ctx<D>& c,
+                                     int j, const bf16x8 (&qf)[D / 16], f32x16 (&s_in)[kBC / 32],
+                                     f32x16 (&s_out)[kBC / 32], const bf16x8 (&p_in)[kBC / 16],
+                                     bf16x8 (&p_out)[kBC / 16], RowState<D>& st) {
   using G = Geom<D>;
   constexpr int kCt = D / 32, kKs = kBC / 16, kKb = kBC / 32, kDs = D / 16;
   constexpr int kPV = kKs * kCt;        // P V steps: (t, ct), ct fastest
   constexpr int kS = kDs * kKb;         // S steps: (ks, kb), kb fastest
-  constexpr int kSteps = kPV + kS;
-  constexpr int kAhead = 8;
-  bf16x8 opnd[kSteps];
-  auto fetch = [&](int i) {
-    if (i < kPV) {
-      const int t = i / kCt, ct = i % kCt;
-      const char* p = v_read + c.v_lane + t * 16 * G::kVStride + ct * 64;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * G::kVStride));
-      opnd[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    } else {
-      const int ks = (i - kPV) / kKb, kb = (i - kPV) % kKb;
-      opnd[i] = *reinterpret_cast<const bf16x8*>(k_read + c.k_lane + kb * 32 * G::kKStride + ks * 32);
-    }
+  static_assert(kPV == kS, "P V and S step counts are interleaved one to one");
+  constexpr int kAhead = 2;             // step pairs whose operands are requested ahead
+
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of K_{j+1}, V_{j-1}
+  __builtin_amdgcn_s_barrier();                      // ... and everyone's; j-1's reads done
+  __builtin_amdgcn_sched_barrier(0);
+
+  bf16x8 v_op[kPV], k_op[kS];
+  auto fetch = [&](int i) {             // operands of P V step i and S step i
+    const int t = i / kCt, ct = i % kCt;
+    v_op[i] = v_operand<D>(v_read, c.v_off[ct], t);
+    const int ks = i / kKb, kb = i % kKb;
+    k_op[i] = *reinterpret_cast<const bf16x8*>(k_read + c.k_off[ks] + kb * 32 * G::kRowBytes);
   };
   auto mfma = [&](int i) {
-    if (i < kPV) {
-      const int t = i / kCt, ct = i % kCt;
-      st.acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i], pf[t], st.acc[ct], 0, 0, 0);
-    } else {
-      const int ks = (i - kPV) / kKb, kb = (i - kPV) % kKb;
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i], qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
-    }
+    const int t = i / kCt, ct = i % kCt;
+    st.acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_op[i], p_in[t], st.acc[ct], 0, 0, 0);
+    const int ks = i / kKb, kb = i % kKb;
+    s_out[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_op[i], qf[ks], ks == 0 ? f32x16{} : s_out[kb], 0, 0, 0);
   };
-  static_assert(kPV >= kAhead && kS >= kAhead, "pipeline deeper than a phase");
-  // Scheduling groups (mask 0x100: LDS reads, 0x008: MFMA) pin the order.
+  // The copies of K_{j+2} (into K_j's buffer) and V_j (into V_{j-2}'s) go
+  // out between the MFMA pairs: a copy instruction holds up its wave for tens
+  // of cycles at issue, which the MFMAs already in the pipe cover.
+  constexpr int kCopies = 2 * G::kLoads;
+  constexpr int kCopyEvery = kPV / kCopies;
+  auto copy = [&](int q) {
+    if (q < G::kLoads) c.kcopy.issue(c.Kh, (j + 2) * kBC, c.N, k_fill, c.wave, q);
+    else c.vcopy.issue(c.Vh, j * kBC, c.N, v_fill, c.wave, q - G::kLoads);
+  };
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) fetch(i);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
 #pragma unroll
-  for (int i = 0; i < kPV - kAhead; ++i) {          // P V steps, prefetching P V operands
-    fetch(i + kAhead);
+  for (int i = 0; i < kPV; ++i) {
+    if (i + kAhead < kPV) fetch(i + kAhead);
     mfma(i);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i % kCopyEvery == 1) copy(i / kCopyEvery);
   }
+  bool rescale;
+  const float alpha = softmax_tile<D, MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st, p_out, &rescale);
+  // Interleave: each step pair is one MFMA pair, its operand reads and an
+  // equal share of the softmax's VALU work (mask 0x008 MFMA, 0x100 LDS read,
+  // 0x002 VALU, 0x010 VMEM).
+  __builtin_amdgcn_sched_group_barrier(0x100, 3 * kAhead, 0);
 #pragma unroll
-  for (int i = kPV - kAhead; i < kSteps - kAhead; ++i) {   // prefetching S operands
-    fetch(i + kAhead);
-    mfma(i);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  for (int i = 0; i < kPV; ++i) {
+    if (i + kAhead < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    if (i % kCopyEvery == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
   }
+  if (rescale) {
 #pragma unroll
-  for (int i = kSteps - kAhead; i < kSteps; ++i) {
-    mfma(i);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[ct][r] *= alpha;
   }
 }
 
-// The two groups' schedules.  Slots are separated by workgroup barriers;
-// group 0 runs MFMA blocks in even slots and VALU blocks in odd slots, group 1
-// the opposite, so on every SIMD (one wave of each group) the matrix unit
-// works on one wave's products while the other wave does its softmax.
-//   group 0:  S_0 | V(0) | M(0) | V(1) | M(1) | ... | V(n-1) | M(n-1) | -
-//   group 1:   -  | S_0  | V(0) | M(0) | V(1) | ... | M(n-2) | V(n-1) | M(n-1)
-// K_j is read in slots 2j, 2j+1 and V_j in 2j+2, 2j+3, so the copies of
-// K_{j+2} and V_{j+1} start at slot 2j+2 and are waited for at the end of
-// slot 2j+3.  A period's four buffers (K_{j+1}, V_j read; K_j's and V_{j-1}'s
-// being refilled) are distinct restrict pointers: that lets the compiler keep
-// the copies in flight across the LDS reads; the explicit waits order them.
+// Two steps with constant LDS parity, S/P register sets swapped between them.
 template <int D, bool MASKED>
-__device__ __forceinline__ void period_g0(const Ctx<D>& c, int j, const char* __restrict__ k_read,
-                                          const char* __restrict__ v_read, char* __restrict__ k_fill,
-                                          char* __restrict__ v_fill, const bf16x8 (&qf)[D / 16],
-                                          f32x16 (&s)[kBC / 32], bf16x8 (&pf)[kBC / 16], RowState<D>& st) {
-  slot_barrier();                          // slot 2j+1
-  softmax_tile<D, MASKED>(s, j * kBC, c.lim, c.h, c.c_log2, st, pf);
-  if (j > 0) wait_copies();                // copies started at slot 2j
-  slot_barrier();                          // slot 2j+2
-  issue_copies<D>(c, j, k_fill, v_fill);
-  mfma_block<D>(c, k_read, v_read, qf, pf, s, st);
-}
-
-template <int D, bool MASKED>
-__device__ __forceinline__ void period_g1(const Ctx<D>& c, int j, const char* __restrict__ k_read,
-                                          const char* __restrict__ v_read, char* __restrict__ k_fill,
-                                          char* __restrict__ v_fill, const bf16x8 (&qf)[D / 16],
-                                          f32x16 (&s)[kBC / 32], bf16x8 (&pf)[kBC / 16], RowState<D>& st) {
-  slot_barrier();                          // slot 2j+2
-  issue_copies<D>(c, j, k_fill, v_fill);
-  softmax_tile<D, MASKED>(s, j * kBC, c.lim, c.h, c.c_log2, st, pf);
-  slot_barrier();                          // slot 2j+3
-  mfma_block<D>(c, k_read, v_read, qf, pf, s, st);
-  wait_copies();
-}
-
-// Run period j of group G: buffers by the parity of j.
-template <int D, int G, bool MASKED>
-__device__ __forceinline__ void period(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
-                                       f32x16 (&s)[kBC / 32], bf16x8 (&pf)[kBC / 16], RowState<D>& st) {
-  using Gm = Geom<D>;
-  const int par = j & 1;
-  char* k_same = c.lds + par * Gm::kKTile;                        // K_j's buffer
-  char* k_other = c.lds + (par ^ 1) * Gm::kKTile;                 // K_{j+1}
-  char* v_same = c.lds + 2 * Gm::kKTile + par * Gm::kVTile;       // V_j
-  char* v_other = c.lds + 2 * Gm::kKTile + (par ^ 1) * Gm::kVTile;  // V_{j-1}, refilled with V_{j+1}
-  if (G == 0) period_g0<D, MASKED>(c, j, k_other, v_same, k_same, v_other, qf, s, pf, st);
-  else        period_g1<D, MASKED>(c, j, k_other, v_same, k_same, v_other, qf, s, pf, st);
+__device__ __forceinline__ void step_pair(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&sa)[kBC / 32], f32x16 (&sb)[kBC / 32],
+                                          bf16x8 (&pa)[kBC / 16], bf16x8 (&pb)[kBC / 16], RowState<D>& st) {
+  using G = Geom<D>;
+  // j even: read K buffer 1 and V buffer 1, fill K buffer 0 and V buffer 0
+  step<D, MASKED>(c.lds + G::kKOff1, c.lds + G::kVOff1, c.lds + G::kKOff0, c.lds + G::kVOff0, c, j, qf,
+                  sa, sb, pa, pb, st);
+  step<D, MASKED>(c.lds + G::kKOff0, c.lds + G::kVOff0, c.lds + G::kKOff1, c.lds + G::kVOff1, c, j + 1, qf,
+                  sb, sa, pb, pa, st);
 }
 
 template <int D, bool CAUSAL>
@@ -409,7 +378,6 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   c.h = lane >> 5;                  // which half of the 64 lanes
   const int l32 = lane & 31;        // this lane's query row within the wave
-  const int group = c.wave / kGroupWaves;
 
   // ---- workgroup -> (head, query block)
   const int wg = blockIdx.x;
@@ -436,15 +404,28 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   j_mask = min(j_mask, c.n_tiles);
 
   // ---- per-lane offsets
-  c.k_lane = l32 * G::kKStride + c.h * 16;
-  c.v_lane = (4 * c.h + ((lane & 15) >> 2)) * G::kVStride + (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+#pragma unroll
+  for (int ks = 0; ks < kDs; ++ks)
+    c.k_off[ks] = l32 * G::kRowBytes + (((2 * ks + c.h) ^ G::fk(l32)) << 4);
+  {
+    const int a = lane & 15, cg = (lane >> 4) & 1;
+    const int row = 4 * c.h + (a >> 2);
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+      c.v_off[ct] = row * G::kRowBytes + (((4 * ct + 2 * cg + ((a & 3) >> 1)) ^ G::fv(row)) << 4) + 8 * (a & 1);
+  }
   c.kcopy.init(c.wave, lane);
   c.vcopy.init(c.wave, lane);
 
-  // ---- prologue: K_0, V_0, K_1 in flight while Q is fetched
-  c.kcopy.issue(c.Kh, 0, N, lds + G::kKOff[0], c.wave);
-  c.vcopy.issue(c.Vh, 0, N, lds + G::kVOff[0], c.wave);
-  if (c.n_tiles > 1) c.kcopy.issue(c.Kh, kBC, N, lds + G::kKOff[1], c.wave);
+  // ---- prologue: K_0 and K_1 in flight while Q is fetched; V buffer 1 (read
+  // as "V_{-1}" by step 0, with P_{-1} = 0) is zero-filled.
+#pragma unroll
+  for (int i = 0; i < G::kLoads; ++i) {
+    c.kcopy.issue(c.Kh, 0, N, lds + G::kKOff0, c.wave, i);
+    c.kcopy.issue(c.Kh, kBC, N, lds + G::kKOff1, c.wave, i);
+  }
+  for (int i = tid; i < G::kTile / 8; i += kThreads)
+    reinterpret_cast<u32x2*>(lds + G::kVOff1)[i] = u32x2{0u, 0u};
 
   // Q^T operand: lane holds Q[qrow][16*ks + 8*h .. +7] for each k-step
   bf16x8 qf[kDs];
@@ -464,27 +445,42 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int ct = 0; ct < kCt; ++ct) st.acc[ct] = f32x16{};
   st.m_ref = -INFINITY;
   st.l_part = 0.f;
-  f32x16 s[kBC / 32];
-  bf16x8 pf[kBC / 16];
+  f32x16 sa[kBC / 32], sb[kBC / 32];
+  bf16x8 pa[kBC / 16], pb[kBC / 16];
+#pragma unroll
+  for (int t = 0; t < kBC / 16; ++t) pa[t] = bf16x8{};
 
-  wait_copies();
-  slot_barrier();                                 // slot 0
-  if (group == 0) {
-    scores<D>(lds + G::kKOff[0], c.k_lane, qf, s);
-    int j = 0;
-    for (; j < j_mask; ++j) period<D, 0, false>(c, j, qf, s, pf, st);
-    for (; j < c.n_tiles; ++j) period<D, 0, true>(c, j, qf, s, pf, st);
-    slot_barrier();                               // slot 2n+1: idle
-  } else {
-    slot_barrier();                               // slot 1
-    scores<D>(lds + G::kKOff[0], c.k_lane, qf, s);
-    int j = 0;
-    for (; j < j_mask; ++j) period<D, 1, false>(c, j, qf, s, pf, st);
-    for (; j < c.n_tiles; ++j) period<D, 1, true>(c, j, qf, s, pf, st);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  scores<D>(lds + G::kKOff0, c.k_off, qf, sa);       // S_0
+
+  // ---- main loop, two steps per trip so the LDS parity is a constant
+  int j = 0;
+  const int j_fast = min(j_mask, c.n_tiles);           // tiles [0, j_fast) need no mask
+  for (; j + 2 <= j_fast; j += 2) step_pair<D, false>(c, j, qf, sa, sb, pa, pb, st);
+  for (; j + 2 <= c.n_tiles; j += 2) step_pair<D, true>(c, j, qf, sa, sb, pa, pb, st);
+  if (j < c.n_tiles) {     // odd tile count: one more step, parity 0, then P_{n-1} is in pb
+    step<D, true>(lds + G::kKOff1, lds + G::kVOff1, lds + G::kKOff0, lds + G::kVOff0, c, j, qf, sa, sb,
+                  pa, pb, st);
+    ++j;
+  }
+  // ---- O += V_{n-1} P_{n-1}: V_{n-1} is in buffer (n-1) & 1
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  {
+    const int last = c.n_tiles - 1;
+    const char* vt = lds + ((last & 1) ? G::kVOff1 : G::kVOff0);
+    const bf16x8 (&pl)[kBC / 16] = (c.n_tiles & 1) ? pb : pa;
+#pragma unroll
+    for (int t = 0; t < kBC / 16; ++t)
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct)
+        st.acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt, c.v_off[ct], t), pl[t],
+                                                             st.acc[ct], 0, 0, 0);
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m_ref + log2 l) * ln 2
-  const float l_tot = st.l_part + __shfl_xor(st.l_part, 32);
+  const float l_tot = sum_halves(st.l_part);
   if (qrow < N) {
     const float inv = 1.0f / l_tot;
     __bf16* orow = O + head_off + (size_t)qrow * D;

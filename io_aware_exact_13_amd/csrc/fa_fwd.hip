@@ -29,12 +29,15 @@
 //     permutation by ds_read_b64_tr_b16, which reads V in its natural
 //     row-major LDS layout and hands each lane 4 consecutive keys of one
 //     column.
-//   * K and V tiles go HBM -> LDS with global_load_lds_dwordx4 (no VGPR
-//     staging), double buffered: the loads of tile j+1 are in flight while
-//     tile j is computed; one workgroup barrier per tile.
-//   * LDS rows are XOR-swizzled in 16-byte chunks so that the 32 rows read
-//     by one MFMA operand fetch and the 4-row groups of the transposed reads
-//     spread over all banks.
+//   * Workgroup: 8 waves (two per SIMD) of 32 query rows each, 256 rows;
+//     K/V tiles of 64 keys.  K and V go HBM -> LDS with buffer_load ... lds
+//     (no VGPR staging; the buffer's record count zero-fills rows past N),
+//     each in two LDS buffers.  One workgroup barrier per tile.
+//   * Each wave runs a three-stage software pipeline: in step j it issues,
+//     as one interleaved instruction stream, the MFMAs of S_{j+1} = K_{j+1}
+//     Q^T, those of O += V_{j-1} P_{j-1}, and the softmax of tile j
+//     (S_j -> P_j), plus the copies of K_{j+2} and V_j.  The softmax VALU
+//     work then issues under the wave's own MFMAs and the other wave's.
 //   * The softmax works in base 2 with scale*log2(e) folded into one FMA
 //     before v_exp_f32.  The reference maximum is moved only when the row
 //     maximum grows by more than kSlack (2^8), so the 64-register
@@ -68,7 +71,6 @@ constexpr int kBR = kWaves * 32;  // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;    // log2 units the reference max may lag the true max
-constexpr unsigned kNoRecord = 0x80000000u;   // buffer offset past any tile: reads return 0
 
 // LDS geometry: unpadded rows with XOR-swizzled 16-byte chunks, so a tile is
 // exactly 16 KiB (d=128) and every wave copies the same number of 1 KiB
@@ -135,7 +137,7 @@ struct TileCopy {
 __device__ __forceinline__ float max_halves(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  return __builtin_elementwise_maximum(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
 __device__ __forceinline__ float sum_halves(float x) {
@@ -203,8 +205,9 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, i
         if (key > lim) s[kb][r] = -INFINITY;
       }
   }
-  // row max: a three-way tree over this lane's 16 kKb scores (v_max3),
-  // then the other half's
+  // row max: a three-way tree over this lane's 16 kKb scores, then the other
+  // half's.  The IEEE maximum (NaN-propagating) maps to v_maximum3_f32 and,
+  // unlike fmaxf, needs no canonicalising moves of the MFMA results.
   float part[16 * kKb];
 #pragma unroll
   for (int kb = 0; kb < kKb; ++kb)
@@ -220,7 +223,7 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, i
       const float a = part[3 * r];
       const float b = 3 * r + 1 < n ? part[3 * r + 1] : a;
       const float c = 3 * r + 2 < n ? part[3 * r + 2] : a;
-      part[r] = fmaxf(a, fmaxf(b, c));
+      part[r] = __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
     }
     n = m;
   }

@@ -37,7 +37,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # workload: (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "causal_b1h32_n16384_d128": (
-        "a02290f4b75bbff6cbd03ffaf4dfc1ff1ddf0be79dad8611bb5ed0ba7b37d227", 7.32915e5, 1.33120e5),
+        "8151eab7009bfa094d0d92e802319b060d50b37672c2dd7414f84d30001ca7c6", 7.69853e5, 1.33122e5),
 }
 
 

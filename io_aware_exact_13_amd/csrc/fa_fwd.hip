@@ -31,12 +31,13 @@
 //     column.
 //   * Workgroup: 8 waves (two per SIMD) of 32 query rows each, 256 rows;
 //     K/V tiles of 64 keys.  K and V go HBM -> LDS with buffer_load ... lds
-//     (no VGPR staging; the buffer's record count zero-fills rows past N),
-//     each in two LDS buffers.  One workgroup barrier per tile.
+//     (no VGPR staging; the buffer's record count zero-fills rows past the
+//     last key the workgroup can see), each through a ring of four LDS
+//     buffers, copied two steps before use.  One workgroup barrier per tile.
 //   * Each wave runs a three-stage software pipeline: in step j it issues,
 //     as one interleaved instruction stream, the MFMAs of S_{j+1} = K_{j+1}
 //     Q^T, those of O += V_{j-1} P_{j-1}, and the softmax of tile j
-//     (S_j -> P_j), plus the copies of K_{j+2} and V_j.  The softmax VALU
+//     (S_j -> P_j), plus the copies of K_{j+3} and V_{j+1}.  The softmax VALU
 //     work then issues under the wave's own MFMAs and the other wave's.
 //   * The softmax works in base 2 with scale*log2(e) folded into one FMA
 //     before v_exp_f32.  The reference maximum is moved only when the row
@@ -85,9 +86,13 @@ struct Geom {
   static constexpr int kRowBytes = 2 * D;                   // one K or V row
   static constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
   static constexpr int kTile = kBC * kRowBytes;             // one K or V tile
-  static constexpr int kKOff0 = 0, kKOff1 = kTile;          // two K buffers, two V buffers
-  static constexpr int kVOff0 = 2 * kTile, kVOff1 = 3 * kTile;
-  static constexpr int kLdsBytes = 4 * kTile;
+  static constexpr int kRing = 4;                           // LDS buffers per operand
+  static constexpr int kLdsBytes = 2 * kRing * kTile;
+  __host__ __device__ static constexpr int k_buf(int b) { return b * kTile; }            // K buffer b
+  __host__ __device__ static constexpr int v_buf(int b) { return (kRing + b) * kTile; }  // V buffer b
+  // V buffer b relative to the V region, whose start is folded into the
+  // lanes' V read offsets so that every LDS read immediate stays below 64 KiB
+  __host__ __device__ static constexpr int v_rel(int b) { return b * kTile; }
   static constexpr int kLoads = kTile / (kThreads * 16);    // 1 KiB copies per wave per tile
   static_assert(kLoads * kThreads * 16 == kTile, "tile not a whole number of wave copies");
   __host__ __device__ static constexpr int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
@@ -205,9 +210,8 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, i
         if (key > lim) s[kb][r] = -INFINITY;
       }
   }
-  // row max: a three-way tree over this lane's 16 kKb scores, then the other
-  // half's.  The IEEE maximum (NaN-propagating) maps to v_maximum3_f32 and,
-  // unlike fmaxf, needs no canonicalising moves of the MFMA results.
+  // row max: a three-way tree over this lane's 16 kKb scores (v_max3),
+  // then the other half's
   float part[16 * kKb];
 #pragma unroll
   for (int kb = 0; kb < kKb; ++kb)
@@ -261,7 +265,7 @@ struct Ctx {
   const char* Kh;
   const char* Vh;
   char* lds;
-  int N, n_tiles, lim, wave, h;
+  int N, kv_end, n_tiles, lim, wave, h;
   float c_log2;
   int k_off[D / 16];    // lane's LDS offset of its K operand for k-step ks (32-row block 0)
   int v_off[D / 32];    // lane's LDS offset of its first transposed V read for column tile ct
@@ -269,11 +273,11 @@ struct Ctx {
   TileCopy<D, true> vcopy;
 };
 
-// One pipeline step, iteration j on LDS parity PAR = j & 1.  In flight on
-// entry: S_j (fp32, in s_in) and P_{j-1} (bf16, in p_in); K_{j+1} and V_{j-1}
-// have landed in LDS (K in buffer PAR^1, V in buffer PAR^1).  The step
-//   - starts the copies of K_{j+2} (into K_j's buffer PAR) and V_j (into V_{j-2}'s
-//     buffer PAR), read in the next two steps;
+// One pipeline step, iteration j.  In flight on entry: S_j (fp32, in s_in)
+// and P_{j-1} (bf16, in p_in); K_{j+1} and V_{j-1} have landed in LDS (their
+// copies went out two steps earlier).  The step
+//   - starts the copies of K_{j+3} (into K_{j-1}'s buffer) and V_{j+1} (into
+//     V_{j-3}'s buffer), read two steps later;
 //   - runs, as one interleaved instruction stream, the MFMAs of
 //     S_{j+1} = K_{j+1} Q^T and of O += V_{j-1} P_{j-1} together with the
 //     softmax of tile j (S_j -> P_j): the wave's own VALU work issues in the
@@ -296,7 +300,11 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   static_assert(kPV == kS, "P V and S step counts are interleaved one to one");
   constexpr int kAhead = 2;             // step pairs whose operands are requested ahead
 
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of K_{j+1}, V_{j-1}
+  // this wave's copies of K_{j+1}, V_{j-1} (issued two steps ago; the
+  // previous step's copies may still be in flight) ...
+  if constexpr (G::kLoads == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  static_assert(G::kLoads == 1 || G::kLoads == 2, "copy count per step");
   __builtin_amdgcn_s_barrier();                      // ... and everyone's; j-1's reads done
   __builtin_amdgcn_sched_barrier(0);
 
@@ -313,14 +321,14 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
     const int ks = i / kKb, kb = i % kKb;
     s_out[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_op[i], qf[ks], ks == 0 ? f32x16{} : s_out[kb], 0, 0, 0);
   };
-  // The copies of K_{j+2} (into K_j's buffer) and V_j (into V_{j-2}'s) go
-  // out between the MFMA pairs: a copy instruction holds up its wave for tens
-  // of cycles at issue, which the MFMAs already in the pipe cover.
+  // The copies go out between the MFMAs: a copy instruction holds up its
+  // wave for tens of cycles at issue, which the MFMAs already in the pipe
+  // cover.
   constexpr int kCopies = 2 * G::kLoads;
   constexpr int kCopyEvery = kPV / kCopies;
   auto copy = [&](int q) {
-    if (q < G::kLoads) c.kcopy.issue(c.Kh, (j + 2) * kBC, c.N, k_fill, c.wave, q);
-    else c.vcopy.issue(c.Vh, j * kBC, c.N, v_fill, c.wave, q - G::kLoads);
+    if (q < G::kLoads) c.kcopy.issue(c.Kh, (j + 3) * kBC, c.kv_end, k_fill, c.wave, q);
+    else c.vcopy.issue(c.Vh, (j + 1) * kBC, c.kv_end, v_fill, c.wave, q - G::kLoads);
   };
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) fetch(i);
@@ -332,16 +340,18 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   }
   bool rescale;
   const float alpha = softmax_tile<D, MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st, p_out, &rescale);
-  // Interleave: each step pair is one MFMA pair, its operand reads and an
-  // equal share of the softmax's VALU work (mask 0x008 MFMA, 0x100 LDS read,
-  // 0x002 VALU, 0x010 VMEM).
+  // Interleave: each step pair is two MFMAs, its operand reads and an equal
+  // share of the softmax's VALU work between and after them (mask 0x008
+  // MFMA, 0x100 LDS read, 0x002 VALU, 0x010 VMEM).
   __builtin_amdgcn_sched_group_barrier(0x100, 3 * kAhead, 0);
 #pragma unroll
   for (int i = 0; i < kPV; ++i) {
     if (i + kAhead < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i % kCopyEvery == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
   }
   if (rescale) {
 #pragma unroll
@@ -351,17 +361,31 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   }
 }
 
-// Two steps with constant LDS parity, S/P register sets swapped between them.
+// Four steps, one turn of the LDS rings, S/P register sets swapped between
+// steps.  Step j reads K_{j+1} from K buffer (j+1)%4 and V_{j-1} from V
+// buffer (j-1)%4, and fills K buffer (j+3)%4 and V buffer (j+1)%4.
+template <int D, bool MASKED, int PH>
+__device__ __forceinline__ void step_at(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
+                                        f32x16 (&sa)[kBC / 32], f32x16 (&sb)[kBC / 32],
+                                        bf16x8 (&pa)[kBC / 16], bf16x8 (&pb)[kBC / 16], RowState<D>& st) {
+  using G = Geom<D>;
+  constexpr int R = G::kRing;
+  if constexpr (PH % 2 == 0)
+    step<D, MASKED>(c.lds + G::k_buf((PH + 1) % R), c.lds + G::v_rel((PH + R - 1) % R),
+                    c.lds + G::k_buf((PH + 3) % R), c.lds + G::v_buf((PH + 1) % R), c, j, qf, sa, sb, pa, pb, st);
+  else
+    step<D, MASKED>(c.lds + G::k_buf((PH + 1) % R), c.lds + G::v_rel((PH + R - 1) % R),
+                    c.lds + G::k_buf((PH + 3) % R), c.lds + G::v_buf((PH + 1) % R), c, j, qf, sb, sa, pb, pa, st);
+}
+
 template <int D, bool MASKED>
-__device__ __forceinline__ void step_pair(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
+__device__ __forceinline__ void step_quad(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
                                           f32x16 (&sa)[kBC / 32], f32x16 (&sb)[kBC / 32],
                                           bf16x8 (&pa)[kBC / 16], bf16x8 (&pb)[kBC / 16], RowState<D>& st) {
-  using G = Geom<D>;
-  // j even: read K buffer 1 and V buffer 1, fill K buffer 0 and V buffer 0
-  step<D, MASKED>(c.lds + G::kKOff1, c.lds + G::kVOff1, c.lds + G::kKOff0, c.lds + G::kVOff0, c, j, qf,
-                  sa, sb, pa, pb, st);
-  step<D, MASKED>(c.lds + G::kKOff0, c.lds + G::kVOff0, c.lds + G::kKOff1, c.lds + G::kVOff1, c, j + 1, qf,
-                  sb, sa, pb, pa, st);
+  step_at<D, MASKED, 0>(c, j, qf, sa, sb, pa, pb, st);
+  step_at<D, MASKED, 1>(c, j + 1, qf, sa, sb, pa, pb, st);
+  step_at<D, MASKED, 2>(c, j + 2, qf, sa, sb, pa, pb, st);
+  step_at<D, MASKED, 3>(c, j + 3, qf, sa, sb, pa, pb, st);
 }
 
 template <int D, bool CAUSAL>
@@ -400,6 +424,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // ---- key tiles: every wave walks the workgroup's n_tiles (under the causal
   // mask, tiles wholly past a wave's rows are masked out by its softmax).
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
+  c.kv_end = kv_end;
   c.n_tiles = (kv_end + kBC - 1) / kBC;
   // tiles from j_mask on hold keys past the end or past some query of the block
   int j_mask = (N - 1) / kBC;                           // the tile holding key N-1
@@ -415,7 +440,8 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int row = 4 * c.h + (a >> 2);
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
-      c.v_off[ct] = row * G::kRowBytes + (((4 * ct + 2 * cg + ((a & 3) >> 1)) ^ G::fv(row)) << 4) + 8 * (a & 1);
+      c.v_off[ct] = G::v_buf(0) + row * G::kRowBytes + (((4 * ct + 2 * cg + ((a & 3) >> 1)) ^ G::fv(row)) << 4) +
+                    8 * (a & 1);
   }
   c.kcopy.init(c.wave, lane);
   c.vcopy.init(c.wave, lane);
@@ -424,11 +450,16 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // as "V_{-1}" by step 0, with P_{-1} = 0) is zero-filled.
 #pragma unroll
   for (int i = 0; i < G::kLoads; ++i) {
-    c.kcopy.issue(c.Kh, 0, N, lds + G::kKOff0, c.wave, i);
-    c.kcopy.issue(c.Kh, kBC, N, lds + G::kKOff1, c.wave, i);
+    c.kcopy.issue(c.Kh, 0, kv_end, lds + G::k_buf(0), c.wave, i);
+    c.kcopy.issue(c.Kh, kBC, kv_end, lds + G::k_buf(1), c.wave, i);
   }
-  for (int i = tid; i < G::kTile / 8; i += kThreads)
-    reinterpret_cast<u32x2*>(lds + G::kVOff1)[i] = u32x2{0u, 0u};
+#pragma unroll
+  for (int i = 0; i < G::kLoads; ++i) {   // the copies step 1 waits for: K_2 and V_0
+    c.kcopy.issue(c.Kh, 2 * kBC, kv_end, lds + G::k_buf(2), c.wave, i);
+    c.vcopy.issue(c.Vh, 0, kv_end, lds + G::v_buf(0), c.wave, i);
+  }
+  for (int i = tid; i < G::kTile / 8; i += kThreads)   // V_{-1} = 0
+    reinterpret_cast<u32x2*>(lds + G::v_buf(G::kRing - 1))[i] = u32x2{0u, 0u};
 
   // Q^T operand: lane holds Q[qrow][16*ks + 8*h .. +7] for each k-step
   bf16x8 qf[kDs];
@@ -453,26 +484,25 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < kBC / 16; ++t) pa[t] = bf16x8{};
 
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (G::kLoads == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");   // K_0, K_1
+  else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   __syncthreads();
-  scores<D>(lds + G::kKOff0, c.k_off, qf, sa);       // S_0
+  scores<D>(lds + G::k_buf(0), c.k_off, qf, sa);       // S_0
 
-  // ---- main loop, two steps per trip so the LDS parity is a constant
+  // ---- main loop, four steps per trip so the LDS ring positions are constants
   int j = 0;
   const int j_fast = min(j_mask, c.n_tiles);           // tiles [0, j_fast) need no mask
-  for (; j + 2 <= j_fast; j += 2) step_pair<D, false>(c, j, qf, sa, sb, pa, pb, st);
-  for (; j + 2 <= c.n_tiles; j += 2) step_pair<D, true>(c, j, qf, sa, sb, pa, pb, st);
-  if (j < c.n_tiles) {     // odd tile count: one more step, parity 0, then P_{n-1} is in pb
-    step<D, true>(lds + G::kKOff1, lds + G::kVOff1, lds + G::kKOff0, lds + G::kVOff0, c, j, qf, sa, sb,
-                  pa, pb, st);
-    ++j;
-  }
+  for (; j + 4 <= j_fast; j += 4) step_quad<D, false>(c, j, qf, sa, sb, pa, pb, st);
+  for (; j + 4 <= c.n_tiles; j += 4) step_quad<D, true>(c, j, qf, sa, sb, pa, pb, st);
+  if (j < c.n_tiles) step_at<D, true, 0>(c, j++, qf, sa, sb, pa, pb, st);
+  if (j < c.n_tiles) step_at<D, true, 1>(c, j++, qf, sa, sb, pa, pb, st);
+  if (j < c.n_tiles) step_at<D, true, 2>(c, j++, qf, sa, sb, pa, pb, st);
   // ---- O += V_{n-1} P_{n-1}: V_{n-1} is in buffer (n-1) & 1
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   {
     const int last = c.n_tiles - 1;
-    const char* vt = lds + ((last & 1) ? G::kVOff1 : G::kVOff0);
+    const char* vt = lds + G::v_rel(last % G::kRing);
     const bf16x8 (&pl)[kBC / 16] = (c.n_tiles & 1) ? pb : pa;
 #pragma unroll
     for (int t = 0; t < kBC / 16; ++t)

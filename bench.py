@@ -7,7 +7,12 @@ roofline fraction of the dominant (only) kernel against the bf16 dense MFMA
 peak, and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--all]
+                       [--no-cpu-baseline] [--all] [--shape B,H,N,d,causal]
+
+--all also times every named workload and a non-causal N=16384, d=128 run
+(diagnostic: separates the causal overheads) on stderr.  --shape times an
+ad-hoc shape instead of a named workload (used for the HBM-traffic linearity
+check: the same shape at N=8192 and N=16384 should read about 2x, not 4x).
 """
 from __future__ import annotations
 
@@ -37,7 +42,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # workload: (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "causal_b1h32_n16384_d128": (
-        "8151eab7009bfa094d0d92e802319b060d50b37672c2dd7414f84d30001ca7c6", 7.69853e5, 1.33122e5),
+        "715ae409a8716d12139252d3a713e9f95cbccdffc49bc86a16cf9cf72ee53f4d", 3.34934e5, 1.33120e5),
 }
 
 
@@ -56,6 +61,26 @@ def measured_traffic(name):
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def log_sclk(when):
+    """Log the GPU shader clock level the driver reports (stderr; best effort).
+
+    Reads the amdgpu sysfs table (the current level carries a '*'); no other
+    program is started, since a process that has touched the GPU must not
+    exec one.
+    """
+    import glob
+    try:
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            with open(path) as f:
+                cur = [ln.strip() for ln in f if "*" in ln]
+            if cur:
+                log(f"[bench] sclk {when}: {cur[0]} ({path.split('/')[4]})")
+                return
+        log(f"[bench] sclk {when}: not reported")
+    except OSError as e:
+        log(f"[bench] sclk {when}: unreadable ({e.strerror})")
 
 
 def time_workload(w, steps, warmup):
@@ -122,6 +147,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
+    ap.add_argument("--shape", default=None, help="B,H,N,d,causal instead of a named workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 3 times (counter calibration)")
     args = ap.parse_args()
@@ -147,11 +173,18 @@ def main():
         log("[bench] copied 512 MiB three times")
         return
 
-    name = args.workload or workloads.HEADLINE
-    w = workloads.WORKLOADS[name]
+    if args.shape:
+        B, H, N, d, causal = (int(x) for x in args.shape.split(","))
+        w = workloads.custom(B, H, N, d, bool(causal), seed=3)
+        name = w.name
+    else:
+        name = args.workload or workloads.HEADLINE
+        w = workloads.WORKLOADS[name]
     flops = acc.attention_flops(w.B, w.H, w.N, w.d, w.causal)
     log(f"[bench] {name}: warmup {args.warmup}, steps {args.steps}")
+    log_sclk("before")
     total_ms, per = time_workload(w, args.steps, args.warmup)
+    log_sclk("after")
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
     value = flops / (ms_step * 1e-3) / 1e12
@@ -161,8 +194,9 @@ def main():
         f"min {per[0]:.4f} ms -> {value:.1f} TFLOP/s ({100 * value / acc.PEAK_BF16_DENSE_TFLOPS:.1f}% of peak)")
 
     if args.all:
-        for other in workloads.WORKLOAD_ORDER:
-            ow = workloads.WORKLOADS[other]
+        extra = workloads.custom(1, 32, 16384, 128, False, seed=3)
+        for ow in [workloads.WORKLOADS[o] for o in workloads.WORKLOAD_ORDER] + [extra]:
+            other = ow.name
             tms, p = time_workload(ow, max(5, args.steps // 2), 3)
             f = acc.attention_flops(ow.B, ow.H, ow.N, ow.d, ow.causal)
             t = tms / max(5, args.steps // 2)

@@ -44,10 +44,12 @@
 //     maximum grows by more than kSlack (2^8), so the 64-register
 //     accumulator rescale is skipped on most tiles; the result is exact for
 //     any reference value (it cancels in acc / l) and P stays <= 2^8.
-//   * Workgroup order: heads vary fastest, so with B*H a multiple of 8 every
-//     head stays on one XCD (workgroups are dealt round-robin to the 8 XCDs)
-//     and its K/V stream is shared in that XCD's L2.  Under the causal mask
-//     the longest query blocks launch first.
+//   * Workgroup order: workgroups are dealt round-robin to the 8 XCDs, each
+//     with its own L2.  The block index is remapped so that an XCD walks
+//     whole heads one after another: the workgroups running on it at any
+//     time stream the same head's K/V, which then stays in its L2 (reads past
+//     the L2 grow linearly with N).  Under the causal mask a head's longest
+//     query blocks launch first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -69,6 +71,7 @@ constexpr int kBC = 64;           // keys per K/V tile
 constexpr int kWaves = 8;         // waves per workgroup, 32 query rows each
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * 32;  // query rows per workgroup
+constexpr int kXcds = 8;          // accelerator dies; workgroups are dealt to them round-robin
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;    // log2 units the reference max may lag the true max
@@ -406,10 +409,16 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   c.h = lane >> 5;                  // which half of the 64 lanes
   const int l32 = lane & 31;        // this lane's query row within the wave
 
-  // ---- workgroup -> (head, query block)
+  // ---- workgroup -> (head, query block).  Workgroups are dealt round-robin
+  // to the 8 XCDs; the logical index gives each XCD a contiguous run of whole
+  // heads, walked head by head, so the XCD's running workgroups share one
+  // head's K/V stream in its L2.
   const int wg = blockIdx.x;
-  const int bh = wg % BH;
-  const int qb = CAUSAL ? (n_qblocks - 1 - wg / BH) : (wg / BH);
+  const int n_wg = BH * n_qblocks;
+  const int logical = (n_wg % kXcds == 0) ? (wg % kXcds) * (n_wg / kXcds) + wg / kXcds : wg;
+  const int bh = logical / n_qblocks;
+  const int qi = logical % n_qblocks;
+  const int qb = CAUSAL ? (n_qblocks - 1 - qi) : qi;
   const int q0 = qb * kBR;
   const int qrow = q0 + c.wave * 32 + l32;   // this lane's query
   c.N = N;

@@ -41,3 +41,30 @@ def streamed_head(q, k, v, scale, causal, block):
         acc = acc * shrink[:, None] + p @ vb
         m = m_new
     return acc / l[:, None], m + np.log(l), moved_after_first
+
+
+def reference_moves(q, k, scale, causal, block, slack_log2):
+    """Count, per query row, how often a lazily held reference maximum moves
+    after the first key block: the reference (in log2 units of the scaled
+    score) is replaced by the block's row maximum only when that maximum
+    exceeds it by more than `slack_log2`.  slack_log2 = 0 gives the moves of
+    the plain running maximum.  Returns an int array of move counts per row.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    n = q.shape[0]
+    rows = np.arange(n)
+    ref = np.full(n, -np.inf)
+    moves = np.zeros(n, dtype=np.int64)
+    for j0 in range(0, k.shape[0], block):
+        kb = k[j0:j0 + block]
+        s = scale * (q @ kb.T) / np.log(2.0)
+        if causal:
+            keys = np.arange(j0, j0 + kb.shape[0])
+            s = np.where(keys[None, :] <= rows[:, None], s, -np.inf)
+        blk_max = s.max(axis=1)
+        grow = blk_max > ref + slack_log2
+        if j0 > 0:
+            moves += grow
+        ref = np.where(grow, blk_max, ref)
+    return moves

@@ -38,3 +38,24 @@ def test_peaky_keys_structure():
         assert hot == 10
     assert 0.4 < q.float().std().item() < 0.6
     assert 0.4 < v.float().std().item() < 0.6
+
+
+def test_peaky_workload_moves_the_reference_maximum():
+    """The peaky causal workload must exercise the accumulator rescale: count
+    the query rows (first 4096 of head 0, keys in 64-key blocks as the kernel
+    walks them) whose running maximum grows after the first block, and those
+    whose reference moves under a lag of up to 8 in log2 units (the kernel's
+    rule).  Both counts are reported; the second must not be zero."""
+    import numpy as np
+    from streaming_model import reference_moves
+    w = workloads.WORKLOADS["causal_peaky_b1h8_n65536_d128"]
+    q, k, _ = workloads.make_inputs(w)
+    n = 4096
+    qh = q[0, 0, :n].double().numpy()
+    kh = k[0, 0, :n].double().numpy()
+    plain = reference_moves(qh, kh, w.scale, True, 64, 0.0)
+    lazy = reference_moves(qh, kh, w.scale, True, 64, 8.0)
+    print(f"\nrows with a growing maximum after the first tile: {int((plain > 0).sum())} of {n}; "
+          f"rows whose lagging reference moves: {int((lazy > 0).sum())} ({int(lazy.sum())} moves)")
+    assert (plain > 0).sum() > 0
+    assert (lazy > 0).sum() > 0

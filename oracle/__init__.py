@@ -1,4 +1,4 @@
-"""CPU fp64 oracle for the exact attention forward -- TEST INFRASTRUCTURE.
+"""CPU fp64 oracle for exact attention, forward and gradients -- TEST INFRASTRUCTURE.
 
 Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
 may import this package.  The product path (the HIP library and its Python
@@ -10,12 +10,15 @@ Sources cited in this package (pages on IO-aware exact attention):
        (answer.freetools.me)
   [P3] "GPU Kernel 入门：Triton / FlashAttention" (ai.clawlihai.cn)
 
-Pinned by the CPU tests (tests/test_oracle_pins.py): the printed worked
-example of [P3] 动手, brute-force scalar evaluation, an independent library
-softmax, closed forms, invariants.  No function here is "parity unpinned".
+Pinned by the CPU tests (tests/test_oracle_pins.py, tests/test_oracle_bwd_pins.py):
+the printed worked example of [P3] 动手, brute-force scalar evaluation, an
+independent library softmax and autograd, central finite differences of the
+forward, closed forms, invariants.  No function here is "parity unpinned".
 """
 from .attention import (softmax_rows, online_softmax_rows, attention_head_rows,
                         attention, attention_rows, probs_head)
+from .attention_bwd import attention_bwd_head, attention_bwd, attention_bwd_rows
 
 __all__ = ["softmax_rows", "online_softmax_rows", "attention_head_rows", "attention",
-           "attention_rows", "probs_head"]
+           "attention_rows", "probs_head", "attention_bwd_head", "attention_bwd",
+           "attention_bwd_rows"]

@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) fused exact attention forward.
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact attention: forward and
+ * its gradients.
  *
  * The operation is standard scaled dot-product attention computed without
  * writing the N x N score or probability matrices to memory:
@@ -36,10 +37,10 @@ extern "C" {
 #define FA_ERR_SHAPE     -2  /* B, H or N <= 0, or the launch would exceed the grid limit   */
 #define FA_ERR_HEAD_DIM  -3  /* d is not 64 or 128                                          */
 #define FA_ERR_SCALE     -4  /* scale is not a finite number > 0                            */
-#define FA_ERR_ALIGN     -5  /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned  */
+#define FA_ERR_ALIGN     -5  /* a bf16 tensor not 16-byte aligned, or an fp32 one not 4-byte  */
 #define FA_ERR_LAUNCH    -6  /* the HIP launch reported an error                            */
 #define FA_ERR_FLAG      -7  /* causal is not 0 or 1                                        */
-#define FA_ERR_ALIAS     -8  /* an output buffer overlaps an input or the other output      */
+#define FA_ERR_ALIAS     -8  /* an output buffer overlaps an input or another output        */
 
 /*
  * fa_fwd -- enqueue the attention forward on `stream` and return.
@@ -79,6 +80,40 @@ const char* fa_status_str(int status);
  */
 int fa_fwd_tile(int B, int H, int N, int d, int causal,
                 int* rows_per_block, int* keys_per_tile, int* waves, long long* blocks);
+
+/*
+ * fa_bwd -- enqueue the gradients of fa_fwd's output on `stream` and return.
+ *
+ * Source: "为什么Flash Attention能将注意力计算提速数倍而不损失精度", section
+ * 反向传播中的重计算策略: the backward pass recomputes S and P on chip from
+ * Q, K, V (and the per-row statistics the forward kept) instead of storing
+ * them.  What it returns is the plain gradient of O = softmax(scale Q K^T
+ * [mask]) V for an upstream gradient dO:
+ *   P = exp(scale Q K^T - LSE) (masked entries 0), dP = dO V^T,
+ *   D_i = sum_c dO_ic O_ic, dS = P (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+ *
+ * Arguments (all device pointers, allocated and owned by the caller; the
+ * [B][H][N][d] / [B][H][N] layouts are those of fa_fwd):
+ *   q, k, v   bf16 inputs of the forward.  Read only.  16-byte aligned.
+ *   o, lse    the forward's outputs for these q, k, v, scale and causal
+ *             (bf16 O, fp32 natural-log LSE).  Read only.
+ *   dout      bf16 upstream gradient dO, same layout as o.  Read only.
+ *   dq,dk,dv  bf16 gradients, same layout as q; fully overwritten (round to
+ *             nearest even from fp32).  16-byte aligned.
+ *   delta     fp32 [B][H][N] workspace; overwritten with D = rowsum(dO * O).
+ *             4-byte aligned.
+ *   B, H, N, d, scale, causal, stream: as for fa_fwd.
+ *
+ * Behaviour: the host checks of fa_fwd, extended to every pointer; outputs
+ * and the workspace must not overlap the inputs or each other.  Three
+ * kernels run in order on `stream` (D, then dQ, then dK and dV); the call
+ * allocates nothing, does not synchronise and is bitwise reproducible run
+ * to run (no atomics).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,8 +1,9 @@
-"""MI355X-native fused exact attention forward (HIP, gfx950).
+"""MI355X-native fused exact attention, forward and gradients (HIP, gfx950).
 
 Thin ctypes binding over the C ABI in include/fa.h.  Every step of the
-forward runs in the HIP library; this module only marshals arguments.  If the
-library has not been built, calls fail loudly: there is no fallback path.
+computation runs in the HIP library; this module only marshals arguments.
+If the library has not been built, calls fail loudly: there is no fallback
+path.
 """
 from __future__ import annotations
 
@@ -26,8 +27,8 @@ _lib = None
 
 
 class FaError(RuntimeError):
-    def __init__(self, status: int):
-        super().__init__(f"fa_fwd failed with status {status}: {fa_status_str(status)}")
+    def __init__(self, status: int, call: str = "fa_fwd"):
+        super().__init__(f"{call} failed with status {status}: {fa_status_str(status)}")
         self.status = status
 
 
@@ -49,6 +50,8 @@ def load_library():
     lib.fa_fwd_tile.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
                                 ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_longlong)]
     lib.fa_fwd_tile.restype = ci
+    lib.fa_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    lib.fa_bwd.restype = ci
     _lib = lib
     return lib
 
@@ -57,6 +60,12 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int:
     """C-ABI fa_fwd with raw device addresses (ints); returns the status code."""
     return load_library().fa_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale),
                                  int(causal), stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream) -> int:
+    """C-ABI fa_bwd with raw device addresses (ints); returns the status code."""
+    return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d,
+                                 ctypes.c_float(scale), int(causal), stream)
 
 
 def fa_status_str(status: int) -> str:
@@ -104,3 +113,39 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     if st != FA_OK:
         raise FaError(st)
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None, delta=None,
+        stream=None):
+    """Gradients of fwd's output: returns (dq, dk, dv).
+
+    q, k, v, o, dout: bf16 GPU tensors [B, H, N, d], contiguous; lse: the
+    forward's fp32 [B, H, N].  dq, dk, dv (bf16) and the fp32 [B, H, N]
+    workspace delta are allocated with torch unless given.
+    """
+    import torch
+    ts = (q, k, v, o, dout)
+    if any(t.dtype != torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
+        raise TypeError("q, k, v, o, dout must be bfloat16 and lse float32")
+    if not all(t.is_cuda for t in ts + (lse,)):
+        raise ValueError("all tensors must be GPU tensors")
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts) or lse.shape != q.shape[:3]:
+        raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape and lse be [B, H, N]")
+    if not all(t.is_contiguous() for t in ts + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, float(scale),
+                int(bool(causal)), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

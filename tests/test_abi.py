@@ -25,7 +25,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_tile", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_tile", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -85,3 +85,27 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(io_aware_exact_13_amd, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         io_aware_exact_13_amd.load_library()
+
+
+# fa_bwd: fake addresses again; every call is rejected on the host.
+DO, DQ, DK, DV, DL = 6 << 40, 7 << 40, 8 << 40, 9 << 40, 10 << 40
+
+
+def call_bwd(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=1, N=16, d=64,
+             scale=0.125, causal=0):
+    return fa.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_NULL), (dict(lse=0), fa.FA_ERR_NULL), (dict(dout=0), fa.FA_ERR_NULL),
+    (dict(dq=0), fa.FA_ERR_NULL), (dict(dk=0), fa.FA_ERR_NULL), (dict(dv=0), fa.FA_ERR_NULL),
+    (dict(delta=0), fa.FA_ERR_NULL),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(B=1 << 20, H=1 << 20, N=1 << 20), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_HEAD_DIM), (dict(scale=float("nan")), fa.FA_ERR_SCALE),
+    (dict(causal=3), fa.FA_ERR_FLAG),
+    (dict(dout=DO + 8), fa.FA_ERR_ALIGN), (dict(dk=DK + 4), fa.FA_ERR_ALIGN), (dict(delta=DL + 1), fa.FA_ERR_ALIGN),
+    (dict(dq=Q), fa.FA_ERR_ALIAS), (dict(dv=DO + 32), fa.FA_ERR_ALIAS), (dict(delta=L), fa.FA_ERR_ALIAS),
+    (dict(dk=DQ + 16), fa.FA_ERR_ALIAS), (dict(delta=DV), fa.FA_ERR_ALIAS),
+])
+def test_bad_bwd_arguments_are_rejected_on_the_host(lib, kw, code):
+    assert call_bwd(**kw) == code

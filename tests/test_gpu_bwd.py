@@ -1,0 +1,136 @@
+"""The HIP gradients (fa_bwd) against the fp64 oracle's (GPU only).
+
+Bar (no tolerance is fixed for the gradients, so it is derived from the
+arithmetic): the kernels round P and dS to bf16 (8 significant bits, relative
+error <= 2^-8) before the MFMAs and round dQ, dK, dV to bf16 on the way out.
+Each alone moves an element by up to 2^-8 of its size.  In a contraction
+whose terms have random signs (dV = P^T dO, dK = scale dS^T Q, dQ = scale
+dS K) the operand rounding errors add like the terms themselves, so the
+relative error of a result is about the rms relative rounding error of one
+operand, 2^-8 / sqrt(3) = 2.3e-3, plus the output rounding.  Per tensor the
+test requires max|diff| <= 2^-5 max|ref| (8 units of 2^-8) and
+mean|diff| <= 2^-7 mean|ref| (2 units, about 3.5 times the expected mean),
+against the oracle evaluated on the same bf16 inputs and upstream gradient.
+"""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_13_amd as fa
+import oracle
+import workloads
+from gpu_common import announce, device, to64
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 2.0 ** -5
+MEAN_REL = 2.0 ** -7
+
+SMALL = [
+    (1, 1, 256, 64, False),
+    (1, 1, 256, 128, True),
+    (1, 2, 333, 128, False),
+    (2, 1, 300, 64, True),
+    (1, 2, 513, 128, True),
+    (1, 1, 1, 64, False), (1, 1, 1, 128, True),
+    (1, 1, 65, 128, False), (1, 1, 65, 64, True),
+    (3, 1, 129, 128, True),
+]
+
+
+def run_fwd_bwd(q, k, v, do, scale, causal):
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.fwd(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def check_tensor(name, got, ref):
+    diff = np.abs(got - ref)
+    big = float(np.abs(ref).max())
+    mean_ref = float(np.abs(ref).mean())
+    r_max = float(diff.max()) / big if big > 0 else float(diff.max())
+    r_mean = float(diff.mean()) / mean_ref if mean_ref > 0 else float(diff.mean())
+    announce(f"    {name}: max|diff|/max|ref|={r_max:.3e}  mean|diff|/mean|ref|={r_mean:.3e}")
+    assert np.isfinite(got).all(), name
+    assert r_max <= MAX_REL and r_mean <= MEAN_REL, name
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SMALL)
+def test_small_shapes_match_oracle_gradients(B, H, N, d, causal):
+    w = workloads.custom(B, H, N, d, causal, seed=2000 + N + d + int(causal))
+    q, k, v = workloads.make_inputs(w)
+    do = workloads.make_grad(w)
+    announce(f"[bwd-small] {w.name}")
+    _, _, dq, dk, dv = run_fwd_bwd(q, k, v, do, w.scale, causal)
+    rq, rk, rv = oracle.attention_bwd(to64(q), to64(k), to64(v), to64(do), w.scale, causal)
+    if N == 1:
+        # one key: dV = dO exactly (P = 1 rounds to 1), while dQ and dK are
+        # scale dS (K or Q) with dS = P (dP - D) the difference of two fp32
+        # evaluations of one dot product: zero up to fp32 rounding
+        assert np.array_equal(to64(dv), to64(do))
+        assert float(dq.abs().max()) <= 1e-4 and float(dk.abs().max()) <= 1e-4
+        return
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check_tensor(name, to64(got), ref)
+
+
+@pytest.mark.parametrize("name", ["causal_b1h32_n16384_d128", "mid_b4h16_n4096_d128"])
+def test_full_size_gradients_on_sampled_heads(name):
+    """Full sizes; the oracle recomputes two whole heads (all rows) of dK and dV
+    and sampled rows of dQ of two more."""
+    w = workloads.WORKLOADS[name]
+    announce(f"[bwd-full] {name}: generating inputs")
+    q, k, v = workloads.make_inputs(w)
+    do = workloads.make_grad(w)
+    announce(f"[bwd-full] {name}: running fa_fwd + fa_bwd")
+    _, _, dq, dk, dv = run_fwd_bwd(q, k, v, do, w.scale, w.causal)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    for b, h in heads:
+        announce(f"[bwd-full] {name}: oracle head ({b},{h})")
+        rq, rk, rv = oracle.attention_bwd_head(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]),
+                                               w.scale, w.causal)
+        for tn, got, ref in (("dQ", dq[b, h], rq), ("dK", dk[b, h], rk), ("dV", dv[b, h], rv)):
+            check_tensor(f"{tn}[{b},{h}]", to64(got), ref)
+    rng = np.random.default_rng(11)
+    rows = sorted(set(rng.integers(0, w.N, 16).tolist()) | {0, w.N - 1})
+    for b, h in [(0, w.H // 2), (w.B // 2, 1)]:
+        ref = oracle.attention_bwd_rows(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]),
+                                        w.scale, w.causal, rows)
+        got = to64(dq[b, h])[rows]
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        announce(f"    dQ rows of head ({b},{h}): max|diff|/max|ref|={err:.3e}")
+        assert err <= MAX_REL
+
+
+def test_gradient_special_cases():
+    dev = device()
+    w = workloads.custom(1, 2, 200, 128, True, seed=77)
+    q, k, v = workloads.make_inputs(w)
+    do = workloads.make_grad(w)
+    # V = 0: dP = 0 and O = 0, so dS = 0 and dQ, dK vanish exactly
+    _, _, dq, dk, dv = run_fwd_bwd(q, k, torch.zeros_like(v), do, w.scale, True)
+    assert torch.all(dq == 0) and torch.all(dk == 0)
+    # Q = 0 without the mask: dK = scale dS^T Q vanishes exactly; dV rows are all the mean of dO
+    _, _, dq, dk, dv = run_fwd_bwd(torch.zeros_like(q), k, v, do, w.scale, False)
+    assert torch.all(dk == 0)
+    mean_do = to64(do).mean(axis=2, keepdims=True)
+    assert np.abs(to64(dv) - mean_do).max() <= 2.0 ** -7 * np.abs(mean_do).max() + 1e-6
+    # causal row 0 sees one key with weight 1: its dQ row is (nearly) zero
+    _, _, dq, _, _ = run_fwd_bwd(q, k, v, do, w.scale, True)
+    assert float(dq[:, :, 0].abs().max()) <= 1e-3 * float(dq.abs().max())
+    del dev
+
+
+def test_gradients_are_bitwise_deterministic():
+    w = workloads.custom(2, 2, 700, 128, True, seed=78)
+    q, k, v = workloads.make_inputs(w)
+    do = workloads.make_grad(w)
+    a = run_fwd_bwd(q, k, v, do, w.scale, True)[2:]
+    b = run_fwd_bwd(q, k, v, do, w.scale, True)[2:]
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

@@ -96,3 +96,18 @@ def sha256_of(t: torch.Tensor) -> str:
     raw = t.contiguous().view(torch.int16).numpy().tobytes() if t.dtype == torch.bfloat16 \
         else t.contiguous().numpy().tobytes()
     return hashlib.sha256(raw).hexdigest()
+
+
+GRAD_SEED_OFFSET = 7919
+
+
+def make_grad(w: Workload, seed: int | None = None):
+    """The upstream gradient dO for the backward pass: a contiguous CPU bf16
+    tensor [B, H, N, d] of N(0,1) draws (float32, then round to nearest even),
+    from its own CPU generator seeded with the workload's seed plus 7919 (or
+    `seed` plus 7919), so it is independent of Q, K and V."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed((w.seed if seed is None else seed) + GRAD_SEED_OFFSET)
+    x = torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32)
+    return x.to(torch.bfloat16).contiguous()
+

@@ -9,7 +9,9 @@ peak, and the CPU oracle timed on a bounded sample of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--all] [--shape B,H,N,d,causal]
 
---all also times every named workload and a non-causal N=16384, d=128 run
+--bwd measures fa_bwd (dQ, dK, dV from the forward's O and LSE; the three
+kernels of one call) instead of the forward, against 2.5x the forward FLOPs.
+--all also times every named workload, forward and backward, and a non-causal N=16384, d=128 run
 (diagnostic: separates the causal overheads) on stderr.  --shape times an
 ad-hoc shape instead of a named workload (used for the HBM-traffic linearity
 check: the same shape at N=8192 and N=16384 should read about 2x, not 4x).
@@ -28,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS & % of MI355X bf16 MFMA peak at N=16K,d=128 (1 GPU)"
+METRIC_BWD = "attention bwd TFLOPS (5 products, 2.5x fwd FLOPs) & % of MI355X bf16 MFMA peak (1 GPU)"
 
 KERNEL_SOURCE = os.path.join(ROOT, "io_aware_exact_13_amd", "csrc", "fa_fwd.hip")
 
@@ -83,7 +86,10 @@ def log_sclk(when):
         log(f"[bench] sclk {when}: unreadable ({e.strerror})")
 
 
-def time_workload(w, steps, warmup):
+def time_workload(w, steps, warmup, backward=False):
+    """Time `steps` calls of the forward (or, with backward, of fa_bwd on the
+    forward's outputs) with HIP events on the launch stream: returns the total
+    of the timed region and the sorted per-call durations, in ms."""
     import torch
     import io_aware_exact_13_amd as fa
     import workloads
@@ -93,8 +99,20 @@ def time_workload(w, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
+    if backward:
+        do = workloads.make_grad(w).to(dev)
         fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        delta = torch.empty_like(lse)
+
+        def call():
+            fa.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, delta=delta,
+                   stream=stream)
+    else:
+        def call():
+            fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+    for _ in range(warmup):
+        call()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -104,7 +122,7 @@ def time_workload(w, steps, warmup):
     t_begin.record(stream)
     for i in range(steps):
         starts[i].record(stream)
-        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+        call()
         ends[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -113,8 +131,9 @@ def time_workload(w, steps, warmup):
     return total_ms, per
 
 
-def cpu_baseline(w, n_heads=32):
-    """Time the oracle on `n_heads` whole heads of the workload (every query row)."""
+def cpu_baseline(w, n_heads=32, backward=False):
+    """Time the oracle on `n_heads` whole heads of the workload (every query
+    row): the forward, or with backward the gradients."""
     import numpy as np
     import oracle
     import workloads
@@ -126,17 +145,20 @@ def cpu_baseline(w, n_heads=32):
         threads = os.cpu_count()
     n_heads = min(n_heads, w.B * w.H)
     q, k, v = workloads.make_inputs(w)
-    flops = 0.0
+    do = workloads.make_grad(w) if backward else None
     t0 = time.perf_counter()
     for i in range(n_heads):
         b, h = divmod(i, w.H)
-        oracle.attention_head_rows(q[b, h].double().numpy(), k[b, h].double().numpy(),
-                                   v[b, h].double().numpy(), w.scale, w.causal)
+        args = (q[b, h].double().numpy(), k[b, h].double().numpy(), v[b, h].double().numpy())
+        if backward:
+            oracle.attention_bwd_head(*args, do[b, h].double().numpy(), w.scale, w.causal)
+        else:
+            oracle.attention_head_rows(*args, w.scale, w.causal)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.N * w.N * w.d * n_heads / (2.0 if w.causal else 1.0)
+    flops = 4.0 * w.N * w.N * w.d * n_heads / (2.0 if w.causal else 1.0) * (2.5 if backward else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_heads} of {w.B * w.H} heads of {w.name} (all {w.N} query rows each), "
-                      f"fp64 numpy, {dt:.1f} s"}
+                      f"{'gradients, ' if backward else ''}fp64 numpy, {dt:.1f} s"}
 
 
 def main():
@@ -148,6 +170,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
     ap.add_argument("--shape", default=None, help="B,H,N,d,causal instead of a named workload")
+    ap.add_argument("--bwd", action="store_true", help="measure fa_bwd (the gradients) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 3 times (counter calibration)")
     args = ap.parse_args()
@@ -180,10 +203,11 @@ def main():
     else:
         name = args.workload or workloads.HEADLINE
         w = workloads.WORKLOADS[name]
-    flops = acc.attention_flops(w.B, w.H, w.N, w.d, w.causal)
-    log(f"[bench] {name}: warmup {args.warmup}, steps {args.steps}")
+    flop_fn = acc.attention_bwd_flops if args.bwd else acc.attention_flops
+    flops = flop_fn(w.B, w.H, w.N, w.d, w.causal)
+    log(f"[bench] {name}{' backward' if args.bwd else ''}: warmup {args.warmup}, steps {args.steps}")
     log_sclk("before")
-    total_ms, per = time_workload(w, args.steps, args.warmup)
+    total_ms, per = time_workload(w, args.steps, args.warmup, backward=args.bwd)
     log_sclk("after")
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -197,15 +221,17 @@ def main():
         extra = workloads.custom(1, 32, 16384, 128, False, seed=3)
         for ow in [workloads.WORKLOADS[o] for o in workloads.WORKLOAD_ORDER] + [extra]:
             other = ow.name
-            tms, p = time_workload(ow, max(5, args.steps // 2), 3)
-            f = acc.attention_flops(ow.B, ow.H, ow.N, ow.d, ow.causal)
-            t = tms / max(5, args.steps // 2)
-            log(f"[bench-all] {other:32s} {t * 1e3:9.1f} us  {f / (t * 1e-3) / 1e12:7.1f} TFLOP/s "
-                f"{100 * f / (t * 1e-3) / 1e12 / acc.PEAK_BF16_DENSE_TFLOPS:5.1f}%")
+            for bw in (False, True):
+                tms, p = time_workload(ow, max(5, args.steps // 2), 3, backward=bw)
+                f = (acc.attention_bwd_flops if bw else acc.attention_flops)(ow.B, ow.H, ow.N, ow.d, ow.causal)
+                t = tms / max(5, args.steps // 2)
+                log(f"[bench-all] {other:32s} {'bwd' if bw else 'fwd'} {t * 1e3:9.1f} us  "
+                    f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s "
+                    f"{100 * f / (t * 1e-3) / 1e12 / acc.PEAK_BF16_DENSE_TFLOPS:5.1f}%")
 
-    traffic = measured_traffic(name)
+    traffic = None if args.bwd else measured_traffic(name)
     result = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.bwd else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -217,7 +243,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": name, "pass": "bwd" if args.bwd else "fwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "seed": w.seed,
                    "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
                    "launch": {"rows_per_block": rows, "keys_per_tile": keys, "waves": waves,
@@ -229,7 +255,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"] = cpu_baseline(w, n_heads=8 if args.bwd else 32, backward=args.bwd)
     print(json.dumps(result), flush=True)
 
 

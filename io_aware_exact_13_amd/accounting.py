@@ -25,6 +25,12 @@ def attention_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     return f / 2.0 if causal else f
 
 
+def attention_bwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Algorithmic FLOPs of the recomputation backward: five N x N x d
+    products (S again, dP, dV, dQ, dK) against the forward's two, 2.5x."""
+    return 2.5 * attention_flops(B, H, N, d, causal)
+
+
 def compulsory_bytes(B: int, H: int, N: int, d: int, in_bytes: int = 2, out_bytes: int = 2,
                      lse_bytes: int = 4) -> int:
     return B * H * (3 * N * d * in_bytes + N * d * out_bytes + N * lse_bytes)

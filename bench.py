@@ -9,6 +9,8 @@ peak, and the CPU oracle timed on a bounded sample of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--all] [--shape B,H,N,d,causal]
 
+--splitkv S measures fa_fwd_splitkv with S key ranges per query block (-1:
+the library's plan) instead of fa_fwd.
 --bwd measures fa_bwd (dQ, dK, dV from the forward's O and LSE; the three
 kernels of one call) instead of the forward, against 2.5x the forward FLOPs.
 --all also times every named workload, forward and backward, and a non-causal N=16384, d=128 run
@@ -45,7 +47,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # workload: (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "causal_b1h32_n16384_d128": (
-        "715ae409a8716d12139252d3a713e9f95cbccdffc49bc86a16cf9cf72ee53f4d", 3.34934e5, 1.33120e5),
+        "d88f6ea604ee169300a441a80dc5fca3f2e0a15e095fb36057fb68eee82e4e77", 3.52839e5, 1.33120e5),
 }
 
 
@@ -86,7 +88,7 @@ def log_sclk(when):
         log(f"[bench] sclk {when}: unreadable ({e.strerror})")
 
 
-def time_workload(w, steps, warmup, backward=False):
+def time_workload(w, steps, warmup, backward=False, n_splits=0):
     """Time `steps` calls of the forward (or, with backward, of fa_bwd on the
     forward's outputs) with HIP events on the launch stream: returns the total
     of the timed region and the sorted per-call durations, in ms."""
@@ -108,6 +110,13 @@ def time_workload(w, steps, warmup, backward=False):
         def call():
             fa.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, delta=delta,
                    stream=stream)
+    elif n_splits:
+        o_part = torch.empty((n_splits, w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+        lse_part = torch.empty((n_splits, w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def call():
+            fa.fwd_splitkv(q, k, v, scale=w.scale, causal=w.causal, n_splits=n_splits, out=o, lse=lse,
+                           o_part=o_part, lse_part=lse_part, stream=stream)
     else:
         def call():
             fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
@@ -171,6 +180,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
     ap.add_argument("--shape", default=None, help="B,H,N,d,causal instead of a named workload")
     ap.add_argument("--bwd", action="store_true", help="measure fa_bwd (the gradients) instead of the forward")
+    ap.add_argument("--splitkv", type=int, default=0,
+                    help="measure fa_fwd_splitkv with this many key ranges (-1: the library's plan)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 3 times (counter calibration)")
     args = ap.parse_args()
@@ -207,7 +218,10 @@ def main():
     flops = flop_fn(w.B, w.H, w.N, w.d, w.causal)
     log(f"[bench] {name}{' backward' if args.bwd else ''}: warmup {args.warmup}, steps {args.steps}")
     log_sclk("before")
-    total_ms, per = time_workload(w, args.steps, args.warmup, backward=args.bwd)
+    if args.splitkv < 0:
+        args.splitkv = fa.fa_fwd_splitkv_plan(w.B, w.H, w.N, w.d, int(w.causal))[0]
+    total_ms, per = time_workload(w, args.steps, args.warmup, backward=args.bwd,
+                                  n_splits=0 if args.bwd else args.splitkv)
     log_sclk("after")
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -228,8 +242,18 @@ def main():
                 log(f"[bench-all] {other:32s} {'bwd' if bw else 'fwd'} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s "
                     f"{100 * f / (t * 1e-3) / 1e12 / acc.PEAK_BF16_DENSE_TFLOPS:5.1f}%")
+        # split-KV forward where the query blocks under-fill the GPU: one GPU's
+        # share of the 16K causal workload over 8 GPUs (4 heads) and the tiny one
+        for sw in (workloads.custom(1, 4, 16384, 128, True, seed=3), workloads.WORKLOADS["tiny_b1h1_n256_d64"]):
+            plan = fa.fa_fwd_splitkv_plan(sw.B, sw.H, sw.N, sw.d, int(sw.causal))[0]
+            f = acc.attention_flops(sw.B, sw.H, sw.N, sw.d, sw.causal)
+            for ns in sorted({0, 2, plan, 8}):
+                tms, p = time_workload(sw, max(5, args.steps // 2), 3, n_splits=ns)
+                t = tms / max(5, args.steps // 2)
+                log(f"[bench-all] {sw.name:32s} {'fwd' if ns == 0 else f'split{ns}':>7s} {t * 1e3:9.1f} us  "
+                    f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s{'  (plan)' if ns == plan else ''}")
 
-    traffic = None if args.bwd else measured_traffic(name)
+    traffic = None if (args.bwd or args.splitkv) else measured_traffic(name)
     result = {
         "metric": METRIC_BWD if args.bwd else METRIC,
         "value": round(value, 2),
@@ -243,7 +267,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name, "pass": "bwd" if args.bwd else "fwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": name,
+                   "pass": "bwd" if args.bwd else (f"fwd_splitkv{args.splitkv}" if args.splitkv else "fwd"), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "seed": w.seed,
                    "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
                    "launch": {"rows_per_block": rows, "keys_per_tile": keys, "waves": waves,

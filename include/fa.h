@@ -41,6 +41,7 @@ extern "C" {
 #define FA_ERR_LAUNCH    -6  /* the HIP launch reported an error                            */
 #define FA_ERR_FLAG      -7  /* causal is not 0 or 1                                        */
 #define FA_ERR_ALIAS     -8  /* an output buffer overlaps an input or another output        */
+#define FA_ERR_SPLITS    -9  /* n_splits is not between 1 and 64                            */
 
 /*
  * fa_fwd -- enqueue the attention forward on `stream` and return.
@@ -80,6 +81,45 @@ const char* fa_status_str(int status);
  */
 int fa_fwd_tile(int B, int H, int N, int d, int causal,
                 int* rows_per_block, int* keys_per_tile, int* waves, long long* blocks);
+
+/*
+ * fa_fwd_splitkv -- the forward of fa_fwd with each query block's visible key
+ * tiles divided into n_splits contiguous ranges, one workgroup per range,
+ * then merged.  For launches whose B*H*ceil(N/256) query blocks leave the
+ * GPU's 256 compute units under-filled (few heads, or one GPU's share of
+ * heads split over several GPUs), and as the key-range split a sequence-
+ * sharded run would use.
+ *
+ * Source: "为什么Flash Attention能将注意力计算提速数倍而不损失精度", section
+ * 在线Softmax技巧: two blocks of one row, each with its own maximum and
+ * exponential sum, merge exactly into the row's softmax (l = e^{m1-m} l1 +
+ * e^{m2-m} l2, O rescaled by the same factors); the same page's closing
+ * section names Flash Decoding.  Here each range s yields O_s (normalised by
+ * its own sum) and LSE_s, and LSE = log sum_s exp(LSE_s),
+ * O = sum_s exp(LSE_s - LSE) O_s, which is that merge applied n times.
+ *
+ * Arguments: q, k, v, o, lse, B, H, N, d, scale, causal, stream as for fa_fwd
+ * (same results up to fp32 rounding order), and
+ *   n_splits  1 .. 64 key ranges per query block (ranges may be empty when a
+ *             block has fewer key tiles than n_splits; they contribute nothing).
+ *   o_part    fp32 workspace [n_splits][B][H][N][d], 16-byte aligned.
+ *   lse_part  fp32 workspace [n_splits][B][H][N], 4-byte aligned.
+ * Both workspaces are overwritten; outputs and workspaces must not overlap
+ * the inputs or each other.  Two kernels run in order on `stream`; nothing is
+ * allocated; results are bitwise reproducible run to run.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal, int n_splits,
+                   float* o_part, float* lse_part, hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv_plan -- a split count for (B, H, N, d, causal) that gives
+ * about two workgroups per compute unit (1 when fa_fwd alone does), and the
+ * workspace bytes fa_fwd_splitkv needs for it.  Any output pointer may be
+ * NULL.  Returns FA_OK or the FA_ERR_* code fa_fwd would return.  Host only.
+ */
+int fa_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int* n_splits,
+                        size_t* o_part_bytes, size_t* lse_part_bytes);
 
 /*
  * fa_bwd -- enqueue the gradients of fa_fwd's output on `stream` and return.

@@ -22,6 +22,7 @@ FA_ERR_ALIGN = -5
 FA_ERR_LAUNCH = -6
 FA_ERR_FLAG = -7
 FA_ERR_ALIAS = -8
+FA_ERR_SPLITS = -9
 
 _lib = None
 
@@ -52,6 +53,11 @@ def load_library():
     lib.fa_fwd_tile.restype = ci
     lib.fa_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_bwd.restype = ci
+    lib.fa_fwd_splitkv.argtypes = [vp] * 5 + [ci, ci, ci, ci, ctypes.c_float, ci, ci, vp, vp, vp]
+    lib.fa_fwd_splitkv.restype = ci
+    lib.fa_fwd_splitkv_plan.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_size_t),
+                                        ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_fwd_splitkv_plan.restype = ci
     _lib = lib
     return lib
 
@@ -66,6 +72,23 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, 
     """C-ABI fa_bwd with raw device addresses (ints); returns the status code."""
     return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d,
                                  ctypes.c_float(scale), int(causal), stream)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, n_splits, o_part, lse_part, stream) -> int:
+    """C-ABI fa_fwd_splitkv with raw device addresses (ints); returns the status code."""
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), int(causal),
+                                         int(n_splits), o_part, lse_part, stream)
+
+
+def fa_fwd_splitkv_plan(B, H, N, d, causal):
+    """(n_splits, o_part_bytes, lse_part_bytes) the library suggests for this shape."""
+    n = ctypes.c_int()
+    ob, lb = ctypes.c_size_t(), ctypes.c_size_t()
+    st = load_library().fa_fwd_splitkv_plan(B, H, N, d, int(causal), ctypes.byref(n), ctypes.byref(ob),
+                                            ctypes.byref(lb))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv_plan")
+    return n.value, ob.value, lb.value
 
 
 def fa_status_str(status: int) -> str:
@@ -149,3 +172,42 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=None, out=None, lse=None, o_part=None,
+                lse_part=None, stream=None):
+    """Split-KV attention forward on torch tensors: returns (o, lse).
+
+    Same inputs and results as fwd; n_splits defaults to the library's plan.
+    The fp32 workspaces o_part [n_splits, B, H, N, d] and lse_part
+    [n_splits, B, H, N] are allocated with torch unless given.
+    """
+    import torch
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = fa_fwd_splitkv_plan(B, H, N, d, causal)[0]
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if o_part is None:
+        o_part = torch.empty((n_splits, B, H, N, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n_splits, B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                        float(scale), int(bool(causal)), int(n_splits), o_part.data_ptr(), lse_part.data_ptr(),
+                        stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv")
+    return out, lse

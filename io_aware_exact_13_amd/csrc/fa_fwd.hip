@@ -63,6 +63,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
@@ -71,7 +72,8 @@ constexpr int kBC = 64;           // keys per K/V tile
 constexpr int kWaves = 8;         // waves per workgroup, 32 query rows each
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * 32;  // query rows per workgroup
-constexpr int kXcds = 8;          // accelerator dies; workgroups are dealt to them round-robin
+constexpr int kXcds = 8;
+constexpr int kMaxSplits = 64;    // key ranges per query block in the split-KV forward          // accelerator dies; workgroups are dealt to them round-robin
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;    // log2 units the reference max may lag the true max
@@ -391,11 +393,17 @@ __device__ __forceinline__ void step_quad(const Ctx<D>& c, int j, const bf16x8 (
   step_at<D, MASKED, 3>(c, j + 3, qf, sa, sb, pa, pb, st);
 }
 
-template <int D, bool CAUSAL>
+// SPLIT: the workgroup covers one of n_splits contiguous ranges of its query
+// block's visible key tiles and writes an fp32 partial (O_s = acc / l over its
+// keys, LSE_s) to Opart / Lpart ([n_splits][B*H][N][d], [n_splits][B*H][N]);
+// fa_merge_kernel combines them.  Otherwise it covers all the tiles and
+// writes O (bf16) and LSE.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                   int BH, int N, int n_qblocks, float c_log2) {
+                   float* __restrict__ Opart, float* __restrict__ Lpart,
+                   int BH, int N, int n_qblocks, int n_splits, float c_log2) {
   using G = Geom<D>;
   constexpr int kDs = D / 16;
   constexpr int kCt = D / 32;
@@ -414,10 +422,12 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // heads, walked head by head, so the XCD's running workgroups share one
   // head's K/V stream in its L2.
   const int wg = blockIdx.x;
-  const int n_wg = BH * n_qblocks;
+  const int per_head = n_qblocks * (SPLIT ? n_splits : 1);
+  const int n_wg = BH * per_head;
   const int logical = (n_wg % kXcds == 0) ? (wg % kXcds) * (n_wg / kXcds) + wg / kXcds : wg;
-  const int bh = logical / n_qblocks;
-  const int qi = logical % n_qblocks;
+  const int bh = logical / per_head;
+  const int qi = SPLIT ? (logical % per_head) / n_splits : logical % per_head;
+  const int split = SPLIT ? (logical % per_head) % n_splits : 0;
   const int qb = CAUSAL ? (n_qblocks - 1 - qi) : qi;
   const int q0 = qb * kBR;
   const int qrow = q0 + c.wave * 32 + l32;   // this lane's query
@@ -433,12 +443,25 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // ---- key tiles: every wave walks the workgroup's n_tiles (under the causal
   // mask, tiles wholly past a wave's rows are masked out by its softmax).
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
-  c.kv_end = kv_end;
-  c.n_tiles = (kv_end + kBC - 1) / kBC;
+  const int all_tiles = (kv_end + kBC - 1) / kBC;
+  // this workgroup's tiles [j0, n_tiles): all of them, or one split's share
+  const int j0 = SPLIT ? (int)((long long)split * all_tiles / n_splits) : 0;
+  c.n_tiles = SPLIT ? (int)((long long)(split + 1) * all_tiles / n_splits) : all_tiles;
+  c.kv_end = min(kv_end, c.n_tiles * kBC);              // copies past it read zeros, no traffic
   // tiles from j_mask on hold keys past the end or past some query of the block
   int j_mask = (N - 1) / kBC;                           // the tile holding key N-1
   if (CAUSAL) j_mask = min(j_mask, q0 / kBC);           // first tile with a key > q0
   j_mask = min(j_mask, c.n_tiles);
+  const size_t prow = ((size_t)split * BH + bh) * (size_t)N;   // partial row base (SPLIT)
+  if (SPLIT && j0 == c.n_tiles) {                       // an empty share: O_s = 0, LSE_s = -inf
+    if (qrow < N) {
+      float* op = Opart + (prow + qrow) * D;
+#pragma unroll
+      for (int t = 0; t < D / 8; ++t) *reinterpret_cast<f32x4*>(op + 8 * t + 4 * c.h) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c.h == 0) Lpart[prow + qrow] = -INFINITY;
+    }
+    return;
+  }
 
   // ---- per-lane offsets
 #pragma unroll
@@ -459,13 +482,13 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // as "V_{-1}" by step 0, with P_{-1} = 0) is zero-filled.
 #pragma unroll
   for (int i = 0; i < G::kLoads; ++i) {
-    c.kcopy.issue(c.Kh, 0, kv_end, lds + G::k_buf(0), c.wave, i);
-    c.kcopy.issue(c.Kh, kBC, kv_end, lds + G::k_buf(1), c.wave, i);
+    c.kcopy.issue(c.Kh, j0 * kBC, c.kv_end, lds + G::k_buf(0), c.wave, i);
+    c.kcopy.issue(c.Kh, (j0 + 1) * kBC, c.kv_end, lds + G::k_buf(1), c.wave, i);
   }
 #pragma unroll
-  for (int i = 0; i < G::kLoads; ++i) {   // the copies step 1 waits for: K_2 and V_0
-    c.kcopy.issue(c.Kh, 2 * kBC, kv_end, lds + G::k_buf(2), c.wave, i);
-    c.vcopy.issue(c.Vh, 0, kv_end, lds + G::v_buf(0), c.wave, i);
+  for (int i = 0; i < G::kLoads; ++i) {   // the copies step j0+1 waits for: K_{j0+2} and V_{j0}
+    c.kcopy.issue(c.Kh, (j0 + 2) * kBC, c.kv_end, lds + G::k_buf(2), c.wave, i);
+    c.vcopy.issue(c.Vh, j0 * kBC, c.kv_end, lds + G::v_buf(0), c.wave, i);
   }
   for (int i = tid; i < G::kTile / 8; i += kThreads)   // V_{-1} = 0
     reinterpret_cast<u32x2*>(lds + G::v_buf(G::kRing - 1))[i] = u32x2{0u, 0u};
@@ -496,23 +519,24 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   if constexpr (G::kLoads == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");   // K_0, K_1
   else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   __syncthreads();
-  scores<D>(lds + G::k_buf(0), c.k_off, qf, sa);       // S_0
+  scores<D>(lds + G::k_buf(0), c.k_off, qf, sa);       // S_{j0}
 
-  // ---- main loop, four steps per trip so the LDS ring positions are constants
-  int j = 0;
-  const int j_fast = min(j_mask, c.n_tiles);           // tiles [0, j_fast) need no mask
+  // ---- main loop, four steps per trip so the LDS ring positions (tile
+  // j - j0 modulo 4) are constants
+  int j = j0;
+  const int j_fast = max(j0, j_mask);                   // tiles [j0, j_fast) need no mask
   for (; j + 4 <= j_fast; j += 4) step_quad<D, false>(c, j, qf, sa, sb, pa, pb, st);
   for (; j + 4 <= c.n_tiles; j += 4) step_quad<D, true>(c, j, qf, sa, sb, pa, pb, st);
   if (j < c.n_tiles) step_at<D, true, 0>(c, j++, qf, sa, sb, pa, pb, st);
   if (j < c.n_tiles) step_at<D, true, 1>(c, j++, qf, sa, sb, pa, pb, st);
   if (j < c.n_tiles) step_at<D, true, 2>(c, j++, qf, sa, sb, pa, pb, st);
-  // ---- O += V_{n-1} P_{n-1}: V_{n-1} is in buffer (n-1) & 1
+  // ---- O += V_{n-1} P_{n-1}: V_{n-1} is in ring buffer (n-1-j0) % 4
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   {
-    const int last = c.n_tiles - 1;
+    const int last = c.n_tiles - 1 - j0;
     const char* vt = lds + G::v_rel(last % G::kRing);
-    const bf16x8 (&pl)[kBC / 16] = (c.n_tiles & 1) ? pb : pa;
+    const bf16x8 (&pl)[kBC / 16] = ((last + 1) & 1) ? pb : pa;
 #pragma unroll
     for (int t = 0; t < kBC / 16; ++t)
 #pragma unroll
@@ -523,6 +547,22 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m_ref + log2 l) * ln 2
   const float l_tot = sum_halves(st.l_part);
+  if (SPLIT) {
+    // fp32 partial; a row with no visible key in this share has l = 0
+    if (qrow < N) {
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      float* op = Opart + (prow + qrow) * D;
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<f32x4*>(op + ct * 32 + r4 * 8 + c.h * 4) =
+              f32x4{st.acc[ct][r4 * 4] * inv, st.acc[ct][r4 * 4 + 1] * inv, st.acc[ct][r4 * 4 + 2] * inv,
+                    st.acc[ct][r4 * 4 + 3] * inv};
+      if (c.h == 0) Lpart[prow + qrow] = l_tot > 0.f ? (st.m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (qrow < N) {
     const float inv = 1.0f / l_tot;
     __bf16* orow = O + head_off + (size_t)qrow * D;
@@ -544,6 +584,47 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 }
 
+// Merge of n_splits partial results of the same rows over disjoint key
+// ranges: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  This
+// is the two-block merge of the online softmax ("为什么Flash Attention能将注意力
+// 计算提速数倍而不损失精度", 在线Softmax技巧) applied to n blocks at once, with
+// the blocks' statistics folded into their logsumexps.  D/8 lanes per row,
+// 8 columns each.
+template <int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ Opart,
+                                                       const float* __restrict__ Lpart, __bf16* __restrict__ O,
+                                                       float* __restrict__ LSE, long long rows, int n_splits) {
+  constexpr int kLanes = D / 8;
+  constexpr int kRows = 256 / kLanes;
+  const long long row = (long long)blockIdx.x * kRows + threadIdx.x / kLanes;
+  const int c0 = (threadIdx.x % kLanes) * 8;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int sp = 0; sp < n_splits; ++sp) m = fmaxf(m, Lpart[(size_t)sp * rows + row]);
+  float z = 0.f;
+  f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const float ls = Lpart[(size_t)sp * rows + row];
+    const float w = (ls == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+    z += w;
+    const f32x4* src = reinterpret_cast<const f32x4*>(Opart + ((size_t)sp * rows + row) * D + c0);
+    a0 += w * src[0];
+    a1 += w * src[1];
+  }
+  const float inv = 1.0f / z;
+  uint32_t packed[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = (e < 2 ? a0[2 * e] : a1[2 * e - 4]) * inv;
+    const float x1 = (e < 2 ? a0[2 * e + 1] : a1[2 * e - 3]) * inv;
+    packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1) << 16);
+  }
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<u32x4*>(O + row * D + c0) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  if (c0 == 0) LSE[row] = m + log2f(z) * kLn2;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
@@ -562,6 +643,7 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_FLAG: return "causal must be 0 or 1";
     case FA_ERR_ALIAS: return "output buffers overlap an input or each other";
+    case FA_ERR_SPLITS: return "n_splits must be between 1 and 64";
     default: return "unknown status";
   }
 }
@@ -618,12 +700,84 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const __bf16* Vp = static_cast<const __bf16*>(v);
   __bf16* Op = static_cast<__bf16*>(o);
   const dim3 grid((unsigned)blocks), block(kThreads);
+  float* np = nullptr;
   if (d == 128) {
-    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, BH, N, nqb, c_log2);
-    else        hipLaunchKernelGGL((fa_fwd_kernel<128, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, BH, N, nqb, c_log2);
+    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
+    else        hipLaunchKernelGGL((fa_fwd_kernel<128, false, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
   } else {
-    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<64, true>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, BH, N, nqb, c_log2);
-    else        hipLaunchKernelGGL((fa_fwd_kernel<64, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, BH, N, nqb, c_log2);
+    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<64, true, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
+    else        hipLaunchKernelGGL((fa_fwd_kernel<64, false, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int* n_splits,
+                                   size_t* o_part_bytes, size_t* lse_part_bytes) {
+  long long blocks = 0;
+  const int st = check_shape(B, H, N, d, causal, &blocks);
+  if (st != FA_OK) return st;
+  // enough workgroups for two per CU (256 CUs), at most one split per key
+  // tile of the longest query block, at most 16.  More splits balance the
+  // causal block lengths better but cost the fp32 partials' round trip
+  // through HBM (2 n_splits B H N d 4 bytes).
+  const long long tiles = ((long long)N + kBC - 1) / kBC;
+  long long n = (2LL * 256 + blocks - 1) / blocks;
+  n = max(1LL, min(n, min(16LL, tiles)));
+  if (n_splits) *n_splits = (int)n;
+  const size_t rows = (size_t)B * H * (size_t)N;
+  if (o_part_bytes) *o_part_bytes = (size_t)n * rows * d * 4;
+  if (lse_part_bytes) *lse_part_bytes = (size_t)n * rows * 4;
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int N, int d, float scale, int causal, int n_splits,
+                              float* o_part, float* lse_part, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !o_part || !lse_part) return FA_ERR_NULL;
+  long long blocks = 0;
+  const int st = check_shape(B, H, N, d, causal, &blocks);
+  if (st != FA_OK) return st;
+  if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_SPLITS;
+  if (blocks * n_splits * kThreads > 0xffffffffLL) return FA_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                        reinterpret_cast<uintptr_t>(o_part);
+  if ((mis & 15u) != 0 || ((reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(lse_part)) & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const size_t rows = (size_t)B * H * (size_t)N;
+  const size_t tb = rows * d * 2, lb = rows * 4;
+  const size_t ob = (size_t)n_splits * rows * d * 4, pb = (size_t)n_splits * rows * 4;
+  const void* ins[3] = {q, k, v};
+  const void* outs[4] = {o, lse, o_part, lse_part};
+  const size_t out_bytes[4] = {tb, lb, ob, pb};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 3; ++b)
+      if (overlaps(outs[a], out_bytes[a], ins[b], tb)) return FA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
+  }
+
+  const int BH = B * H;
+  const int nqb = (N + kBR - 1) / kBR;
+  const float c_log2 = scale * kLog2e;
+  const __bf16* Q = static_cast<const __bf16*>(q);
+  const __bf16* Kp = static_cast<const __bf16*>(k);
+  const __bf16* Vp = static_cast<const __bf16*>(v);
+  __bf16* Op = static_cast<__bf16*>(o);
+  __bf16* nb = nullptr;
+  float* nl = nullptr;
+  const dim3 grid((unsigned)(blocks * n_splits)), block(kThreads);
+  if (d == 128) {
+    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
+    else        hipLaunchKernelGGL((fa_fwd_kernel<128, false, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
+    hipLaunchKernelGGL((fa_merge_kernel<128>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
+                       o_part, lse_part, Op, lse, (long long)rows, n_splits);
+  } else {
+    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<64, true, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
+    else        hipLaunchKernelGGL((fa_fwd_kernel<64, false, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
+    hipLaunchKernelGGL((fa_merge_kernel<64>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream,
+                       o_part, lse_part, Op, lse, (long long)rows, n_splits);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -25,7 +25,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_tile", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_fwd_tile",
+                                    "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEAD_DIM, fa.FA_ERR_SCALE,
-             fa.FA_ERR_ALIGN, fa.FA_ERR_LAUNCH, fa.FA_ERR_FLAG, fa.FA_ERR_ALIAS]
+             fa.FA_ERR_ALIGN, fa.FA_ERR_LAUNCH, fa.FA_ERR_FLAG, fa.FA_ERR_ALIAS, fa.FA_ERR_SPLITS]
     names = [fa.fa_status_str(c) for c in codes]
     assert names[0] == "ok"
     assert len(set(names)) == len(names)
@@ -109,3 +110,33 @@ def call_bwd(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DL, 
 ])
 def test_bad_bwd_arguments_are_rejected_on_the_host(lib, kw, code):
     assert call_bwd(**kw) == code
+
+
+# fa_fwd_splitkv: fake addresses; every call is rejected on the host.
+OP, LP = 11 << 40, 12 << 40
+
+
+def call_split(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=16, d=64, scale=0.125, causal=0, n_splits=2, o_part=OP,
+               lse_part=LP):
+    return fa.fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, n_splits, o_part, lse_part, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o_part=0), fa.FA_ERR_NULL), (dict(lse_part=0), fa.FA_ERR_NULL), (dict(q=0), fa.FA_ERR_NULL),
+    (dict(n_splits=0), fa.FA_ERR_SPLITS), (dict(n_splits=65), fa.FA_ERR_SPLITS), (dict(n_splits=-3), fa.FA_ERR_SPLITS),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_HEAD_DIM), (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(causal=5), fa.FA_ERR_FLAG), (dict(o_part=OP + 4), fa.FA_ERR_ALIGN), (dict(lse_part=LP + 2), fa.FA_ERR_ALIGN),
+    (dict(o_part=Q), fa.FA_ERR_ALIAS), (dict(lse_part=O), fa.FA_ERR_ALIAS), (dict(lse_part=OP + 64), fa.FA_ERR_ALIAS),
+])
+def test_bad_splitkv_arguments_are_rejected_on_the_host(lib, kw, code):
+    assert call_split(**kw) == code
+
+
+def test_splitkv_plan(lib):
+    # one GPU's share of the 16K causal workload split over 8 GPUs: 4 heads, 256 query blocks
+    n, ob, lb = fa.fa_fwd_splitkv_plan(1, 4, 16384, 128, 1)
+    assert n == 2 and ob == 2 * 4 * 16384 * 128 * 4 and lb == 2 * 4 * 16384 * 4
+    assert fa.fa_fwd_splitkv_plan(1, 32, 16384, 128, 1)[0] == 1      # 2048 blocks fill the GPU
+    assert fa.fa_fwd_splitkv_plan(1, 1, 256, 64, 0)[0] == 4          # one block, four 64-key tiles
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_splitkv_plan(1, 1, 16, 96, 0)

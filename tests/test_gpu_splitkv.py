@@ -1,0 +1,70 @@
+"""The split-KV forward (fa_fwd_splitkv) against the fp64 oracle, with the
+forward's bar: it computes the same function as fa_fwd (GPU only)."""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_13_amd as fa
+import workloads
+from gpu_common import (O_MAX_ABS, O_MEAN_ABS, LSE_MAX_ABS, announce, compare_full, compare_rows, device,
+                        sample_picks, to64)
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (1, 1, 256, 64, False, 4),
+    (1, 2, 333, 128, False, 3),
+    (2, 1, 1000, 64, True, 5),
+    (1, 3, 700, 128, True, 2),
+    (1, 1, 100, 64, True, 7),      # two key tiles, seven ranges: most ranges are empty
+    (1, 1, 1, 128, False, 3),
+    (1, 2, 513, 128, True, 1),
+]
+
+
+def run_split(q, k, v, scale, causal, n_splits):
+    dev = device()
+    o, lse = fa.fwd_splitkv(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal, n_splits=n_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,n_splits", CASES)
+def test_small_shapes_match_oracle(B, H, N, d, causal, n_splits):
+    w = workloads.custom(B, H, N, d, causal, seed=3000 + N + d + n_splits)
+    q, k, v = workloads.make_inputs(w)
+    announce(f"[splitkv] {w.name} n_splits={n_splits}")
+    o, lse = run_split(q, k, v, w.scale, causal, n_splits)
+    mo, me, ml = compare_full(q, k, v, w.scale, causal, o, lse)
+    announce(f"    max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+
+
+def test_one_gpu_share_of_the_16k_causal_workload():
+    """The headline shape with 4 of its 32 heads (one GPU's share over 8 GPUs)
+    at the planned split count: sampled rows against the oracle, and every
+    element against fa_fwd (the same function, another summation order)."""
+    dev = device()
+    w = workloads.custom(1, 4, 16384, 128, True, seed=3)
+    q, k, v = workloads.make_inputs(w)
+    n = fa.fa_fwd_splitkv_plan(1, 4, 16384, 128, 1)[0]
+    announce(f"[splitkv-share] {w.name} n_splits={n}")
+    o, lse = run_split(q, k, v, w.scale, True, n)
+    mo, me, ml = compare_rows(q, k, v, w.scale, True, o.cpu(), lse.cpu(), sample_picks(w, n_heads=4))
+    announce(f"    sampled rows: max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+    o1, lse1 = fa.fwd(q.to(dev), k.to(dev), v.to(dev), scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    d_o = float((o.float() - o1.float()).abs().max())
+    d_l = float((lse - lse1).abs().max())
+    announce(f"    vs fa_fwd: max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
+    assert d_o <= O_MAX_ABS and d_l <= LSE_MAX_ABS
+
+
+def test_splitkv_is_bitwise_deterministic():
+    w = workloads.custom(1, 2, 900, 128, True, seed=91)
+    q, k, v = workloads.make_inputs(w)
+    a = run_split(q, k, v, w.scale, True, 3)
+    b = run_split(q, k, v, w.scale, True, 3)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])

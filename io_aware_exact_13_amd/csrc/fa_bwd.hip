@@ -18,9 +18,12 @@
 //     LDS).  Each output is written by one workgroup: no atomics, and the
 //     result is bitwise reproducible.
 //   * All products run on v_mfma_f32_32x32x16_bf16 with the operand that a
-//     lane owns for the whole loop (Q and dO rows in the dQ kernel, K and V
-//     rows in the dK/dV kernel) held in registers as the B operand, so every
-//     accumulator column is one of the lane's own rows.  P and dS go from the
+//     lane owns for the whole loop as the B operand (Q and dO rows in the dQ
+//     kernel, K and V rows in the dK/dV kernel), so every accumulator column
+//     is one of the lane's own rows.  They sit in registers, except the
+//     dK/dV kernel's K rows, which stay in LDS for the whole kernel: with
+//     them in registers the kernel needs more than 256 registers per lane
+//     and runs one wave per SIMD instead of two.  P and dS go from the
 //     accumulators straight into the next MFMA's B operand (bf16), and the
 //     matching A operand (K^T, dO^T, Q^T) is read with ds_read_b64_tr_b16
 //     from the row-major LDS tile, with the same key/query permutation.
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const __bf16* __restr
 //   P    = exp2(S^T c - LSE log2 e),  dS = P (dP - D)   (masked keys give 0)
 //   dQ^T += K^T dS^T                      (A: K^T by transposed reads; B: dS from registers)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dQ, int BH, int N, int n_qblocks, float c_log2, float scale) {
@@ -210,11 +213,12 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(
 // ---------------------------------------------------------------- dK, dV
 // One workgroup per (head, block of 128 keys); lane l of wave w owns key
 // k0 + 32 w + l % 32.  Per 32-row query tile:
-//   S  = Q K^T,  dP = dO V^T              (A: Q, dO rows from LDS; B: K, V in registers)
+//   S  = Q K^T,  dP = dO V^T              (A: Q, dO rows from LDS; B: K rows
+//                                          from the resident LDS block, V in registers)
 //   P  = exp2(S c - LSE log2 e),  dS = P (dP - D)      (rows past N or above the key give 0)
 //   dV^T += dO^T P,  dK^T += Q^T dS       (A: dO^T, Q^T by transposed reads; B: P, dS)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int N, int n_kblocks, float c_log2,
@@ -223,8 +227,11 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(
   constexpr int kTileBytes = kQTile * 2 * D;
   constexpr int kStatBytes = 512;                        // 64 LSE then 64 D floats
   constexpr int kBufBytes = 2 * kTileBytes + kStatBytes;  // Q tile, dO tile, statistics
+  constexpr int kKBytes = kKBlock * 2 * D;                // the workgroup's K rows, resident
   using Copy = TileCopy<D, kQTile, kThreads>;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kBufBytes];
+  using KCopy = TileCopy<D, kKBlock, kThreads>;
+  __shared__ __attribute__((aligned(1024))) char lds[kKBytes + 2 * kBufBytes];
+  char* const kblk = lds + 2 * kBufBytes;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -255,10 +262,16 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(
       copy_row_stats(Dh, i * kQTile, N, dst + 2 * kTileBytes + 256, lane);
     }
   };
+  {
+    KCopy kc;
+    kc.init(tid);
+#pragma unroll
+    for (int c = 0; c < KCopy::kIssues; ++c)
+      kc.issue(reinterpret_cast<const char*>(K + head_off), k0, N, kblk, tid, c);
+  }
   if (t0 < n_qt) issue_tile(t0, lds);
 
-  bf16x8 kf[kDs], vf[kDs];
-  load_row_operands<D>(K + head_off + (size_t)(kok ? key : 0) * D, kok, h, kf);
+  bf16x8 vf[kDs];
   load_row_operands<D>(V + head_off + (size_t)(kok ? key : 0) * D, kok, h, vf);
 
   f32x16 acc_dk[kCt], acc_dv[kCt];
@@ -277,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kDs; ++ks) {
-      s = mfma32(row_operand<D>(Qt, 0, ks, lane), kf[ks], s);
+      s = mfma32(row_operand<D>(Qt, 0, ks, lane), row_operand<D>(kblk, 32 * wave, ks, lane), s);
       dp = mfma32(row_operand<D>(dOt, 0, ks, lane), vf[ks], dp);
     }
 

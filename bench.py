@@ -11,6 +11,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 --splitkv S measures fa_fwd_splitkv with S key ranges per query block (-1:
 the library's plan) instead of fa_fwd.
+--fa1order measures the K/V-outer loop-order ablation fa_fwd_fa1order.
 --bwd measures fa_bwd (dQ, dK, dV from the forward's O and LSE; the three
 kernels of one call) instead of the forward, against 2.5x the forward FLOPs.
 --all also times every named workload, forward and backward, and a non-causal N=16384, d=128 run
@@ -88,7 +89,7 @@ def log_sclk(when):
         log(f"[bench] sclk {when}: unreadable ({e.strerror})")
 
 
-def time_workload(w, steps, warmup, backward=False, n_splits=0):
+def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False):
     """Time `steps` calls of the forward (or, with backward, of fa_bwd on the
     forward's outputs) with HIP events on the launch stream: returns the total
     of the timed region and the sorted per-call durations, in ms."""
@@ -110,6 +111,14 @@ def time_workload(w, steps, warmup, backward=False, n_splits=0):
         def call():
             fa.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv, delta=delta,
                    stream=stream)
+    elif fa1order:
+        f32 = dict(dtype=torch.float32, device=dev)
+        o_acc = torch.empty((w.B, w.H, w.N, w.d), **f32)
+        m_ws, l_ws = torch.empty_like(lse), torch.empty_like(lse)
+
+        def call():
+            fa.fwd_fa1order(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, o_acc=o_acc, m=m_ws, l=l_ws,
+                            stream=stream)
     elif n_splits:
         o_part = torch.empty((n_splits, w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
         lse_part = torch.empty((n_splits, w.B, w.H, w.N), dtype=torch.float32, device=dev)
@@ -180,6 +189,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
     ap.add_argument("--shape", default=None, help="B,H,N,d,causal instead of a named workload")
     ap.add_argument("--bwd", action="store_true", help="measure fa_bwd (the gradients) instead of the forward")
+    ap.add_argument("--fa1order", action="store_true",
+                    help="measure the K/V-outer loop order ablation (fa_fwd_fa1order) instead of fa_fwd")
     ap.add_argument("--splitkv", type=int, default=0,
                     help="measure fa_fwd_splitkv with this many key ranges (-1: the library's plan)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -221,7 +232,7 @@ def main():
     if args.splitkv < 0:
         args.splitkv = fa.fa_fwd_splitkv_plan(w.B, w.H, w.N, w.d, int(w.causal))[0]
     total_ms, per = time_workload(w, args.steps, args.warmup, backward=args.bwd,
-                                  n_splits=0 if args.bwd else args.splitkv)
+                                  n_splits=0 if args.bwd else args.splitkv, fa1order=args.fa1order)
     log_sclk("after")
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -253,7 +264,7 @@ def main():
                 log(f"[bench-all] {sw.name:32s} {'fwd' if ns == 0 else f'split{ns}':>7s} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s{'  (plan)' if ns == plan else ''}")
 
-    traffic = None if (args.bwd or args.splitkv) else measured_traffic(name)
+    traffic = None if (args.bwd or args.splitkv or args.fa1order) else measured_traffic(name)
     result = {
         "metric": METRIC_BWD if args.bwd else METRIC,
         "value": round(value, 2),
@@ -268,7 +279,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": name,
-                   "pass": "bwd" if args.bwd else (f"fwd_splitkv{args.splitkv}" if args.splitkv else "fwd"), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "pass": "bwd" if args.bwd else ("fwd_fa1order" if args.fa1order else
+                                                   (f"fwd_splitkv{args.splitkv}" if args.splitkv else "fwd")), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "seed": w.seed,
                    "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
                    "launch": {"rows_per_block": rows, "keys_per_tile": keys, "waves": waves,

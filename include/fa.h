@@ -122,6 +122,27 @@ int fa_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int* n_splits,
                         size_t* o_part_bytes, size_t* lse_part_bytes);
 
 /*
+ * fa_fwd_fa1order -- the same forward computed in the other loop order the
+ * pages give, kept as an ablation that measures what that order costs:
+ * K/V blocks in the outer loop, query blocks in the inner one, so every query
+ * block's running output O_i and statistics l_i, m_i go to HBM and back once
+ * per K/V block ("为什么Flash Attention能将注意力计算提速数倍而不损失精度",
+ * section 分块计算(Tiling), the two-loop pseudocode; "FlashAttention的Triton实现：
+ * IO-aware注意力机制底层原理", section FA1 vs FA2).  Not a fast path: one
+ * launch per 64-key block, then one that writes O and LSE.
+ *
+ * Arguments: q, k, v, o, lse, B, H, N, d, scale, causal, stream as for fa_fwd
+ * (same results up to fp32 rounding), and the fp32 workspaces
+ *   o_acc  [B][H][N][d], 16-byte aligned: the running O_i between blocks;
+ *   m, l   [B][H][N], 4-byte aligned: the running statistics.
+ * All are overwritten; outputs and workspaces must not overlap the inputs or
+ * each other.  Nothing is allocated; results are reproducible run to run.
+ */
+int fa_fwd_fa1order(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    float* o_acc, float* m, float* l, hipStream_t stream);
+
+/*
  * fa_bwd -- enqueue the gradients of fa_fwd's output on `stream` and return.
  *
  * Source: "为什么Flash Attention能将注意力计算提速数倍而不损失精度", section

@@ -58,6 +58,8 @@ def load_library():
     lib.fa_fwd_splitkv_plan.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_size_t),
                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_fwd_splitkv_plan.restype = ci
+    lib.fa_fwd_fa1order.argtypes = [vp] * 5 + [ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, vp, vp]
+    lib.fa_fwd_fa1order.restype = ci
     _lib = lib
     return lib
 
@@ -89,6 +91,12 @@ def fa_fwd_splitkv_plan(B, H, N, d, causal):
     if st != FA_OK:
         raise FaError(st, "fa_fwd_splitkv_plan")
     return n.value, ob.value, lb.value
+
+
+def fa_fwd_fa1order(q, k, v, o, lse, B, H, N, d, scale, causal, o_acc, m, l, stream) -> int:
+    """C-ABI fa_fwd_fa1order with raw device addresses (ints); returns the status code."""
+    return load_library().fa_fwd_fa1order(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), int(causal),
+                                          o_acc, m, l, stream)
 
 
 def fa_status_str(status: int) -> str:
@@ -210,4 +218,34 @@ def fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=None, out=None, lse=
                         stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+def fwd_fa1order(q, k, v, scale=None, causal=False, out=None, lse=None, o_acc=None, m=None, l=None, stream=None):
+    """The forward in the K/V-outer (FA1) loop order, an ablation: returns (o, lse).
+    The fp32 workspaces o_acc [B, H, N, d], m and l [B, H, N] are allocated
+    with torch unless given."""
+    import torch
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    f32 = dict(dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, N), **f32) if lse is None else lse
+    o_acc = torch.empty((B, H, N, d), **f32) if o_acc is None else o_acc
+    m = torch.empty((B, H, N), **f32) if m is None else m
+    l = torch.empty((B, H, N), **f32) if l is None else l
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_fa1order(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                         float(scale), int(bool(causal)), o_acc.data_ptr(), m.data_ptr(), l.data_ptr(),
+                         stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fa1order")
     return out, lse

@@ -25,8 +25,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_fwd_tile",
-                                    "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_fa1order", "fa_fwd_splitkv", "fa_fwd_splitkv_plan",
+                                    "fa_fwd_tile", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -140,3 +140,21 @@ def test_splitkv_plan(lib):
     assert fa.fa_fwd_splitkv_plan(1, 1, 256, 64, 0)[0] == 4          # one block, four 64-key tiles
     with pytest.raises(fa.FaError):
         fa.fa_fwd_splitkv_plan(1, 1, 16, 96, 0)
+
+
+# fa_fwd_fa1order: fake addresses; every call is rejected on the host.
+OA, MW, LW = 13 << 40, 14 << 40, 15 << 40
+
+
+def call_fa1(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=16, d=64, scale=0.125, causal=0, o_acc=OA, m=MW, l=LW):
+    return fa.fa_fwd_fa1order(q, k, v, o, lse, B, H, N, d, scale, causal, o_acc, m, l, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o_acc=0), fa.FA_ERR_NULL), (dict(m=0), fa.FA_ERR_NULL), (dict(l=0), fa.FA_ERR_NULL),
+    (dict(N=0), fa.FA_ERR_SHAPE), (dict(d=80), fa.FA_ERR_HEAD_DIM), (dict(scale=-1.0), fa.FA_ERR_SCALE),
+    (dict(causal=2), fa.FA_ERR_FLAG), (dict(o_acc=OA + 8), fa.FA_ERR_ALIGN), (dict(m=MW + 1), fa.FA_ERR_ALIGN),
+    (dict(o_acc=K), fa.FA_ERR_ALIAS), (dict(l=MW), fa.FA_ERR_ALIAS), (dict(m=O + 64), fa.FA_ERR_ALIAS),
+])
+def test_bad_fa1order_arguments_are_rejected_on_the_host(lib, kw, code):
+    assert call_fa1(**kw) == code

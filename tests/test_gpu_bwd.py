@@ -134,3 +134,17 @@ def test_gradients_are_bitwise_deterministic():
     b = run_fwd_bwd(q, k, v, do, w.scale, True)[2:]
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_long_sequence_gradients():
+    """A 32K-token causal head: dK and dV of the whole head and sampled dQ rows."""
+    w = workloads.custom(1, 1, 32768, 128, True, seed=5100)
+    q, k, v = workloads.make_inputs(w)
+    do = workloads.make_grad(w)
+    announce(f"[bwd-long] {w.name}: running fa_fwd + fa_bwd")
+    _, _, dq, dk, dv = run_fwd_bwd(q, k, v, do, w.scale, True)
+    announce(f"[bwd-long] {w.name}: oracle")
+    rq, rk, rv = oracle.attention_bwd_head(to64(q[0, 0]), to64(k[0, 0]), to64(v[0, 0]), to64(do[0, 0]), w.scale,
+                                           True)
+    for tn, got, ref in (("dQ", dq[0, 0], rq), ("dK", dk[0, 0], rk), ("dV", dv[0, 0], rv)):
+        check_tensor(tn, to64(got), ref)

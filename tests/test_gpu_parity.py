@@ -146,3 +146,19 @@ def test_non_default_scale_and_large_scores():
         announce(f"[scale {scale} x{mult}] max|dO|={raw:.3e} (beyond O's rounding {beyond:.3e}) "
                  f"mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
         assert beyond <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 1, 262144, 128, True), (1, 2, 131072, 64, False)])
+def test_long_sequences_on_sampled_rows(B, H, N, d, causal):
+    """Sequences 4x and 2x the longest workload's: 32-bit tile and row
+    arithmetic, the causal block order and the reference-maximum path over
+    thousands of key tiles.  Sampled rows against the oracle."""
+    w = workloads.custom(B, H, N, d, causal, seed=5000 + d)
+    announce(f"[parity-long] {w.name}: generating inputs")
+    q, k, v = workloads.make_inputs(w)
+    announce(f"[parity-long] {w.name}: running fa_fwd")
+    o, lse = run_gpu(q, k, v, w.scale, causal)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    mo, me, ml = compare_rows(q, k, v, w.scale, causal, o.cpu(), lse.cpu(), sample_picks(w, n_heads=2, n_rand=24))
+    announce(f"    max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS

@@ -48,7 +48,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # workload: (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "causal_b1h32_n16384_d128": (
-        "d88f6ea604ee169300a441a80dc5fca3f2e0a15e095fb36057fb68eee82e4e77", 3.52839e5, 1.33120e5),
+        "463bd7e11e13c6d0f99443af08ca97264f47c34b21a0366b9131b282b22dff65", 3.43241e5, 1.33120e5),
 }
 
 

@@ -40,10 +40,15 @@
 //     (S_j -> P_j), plus the copies of K_{j+3} and V_{j+1}.  The softmax VALU
 //     work then issues under the wave's own MFMAs and the other wave's.
 //   * The softmax works in base 2 with scale*log2(e) folded into one FMA
-//     before v_exp_f32.  The reference maximum is moved only when the row
-//     maximum grows by more than kSlack (2^8), so the 64-register
-//     accumulator rescale is skipped on most tiles; the result is exact for
-//     any reference value (it cancels in acc / l) and P stays <= 2^8.
+//     before v_exp_f32.  Any reference maximum gives the same acc / l, so
+//     the reference lags the true row maximum: for d = 128 it moves only
+//     when the tile's row maximum exceeds it by more than kSlack (2^8), so
+//     the accumulator rescale is skipped on most tiles.  For d = 64, where
+//     the MFMA work per tile halves and the softmax's VALU work does not,
+//     not even the row maximum is formed: P is taken against the current
+//     reference, and only if a lane's tile sum of P passes kPMax (2^32; also
+//     the first tile, where the reference is -inf) does the wave redo the
+//     tile with the true maximum.
 //   * Workgroup order: workgroups are dealt round-robin to the 8 XCDs, each
 //     with its own L2.  The block index is remapped so that an XCD walks
 //     whole heads one after another: the workgroups running on it at any
@@ -76,6 +81,7 @@ constexpr int kXcds = 8;
 constexpr int kMaxSplits = 64;    // key ranges per query block in the split-KV forward          // accelerator dies; workgroups are dealt to them round-robin
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kPMax = 4294967296.0f;   // 2^32: largest tile sum of P a lane may reach before the reference moves
 constexpr float kSlack = 8.0f;    // log2 units the reference max may lag the true max
 
 // LDS geometry: unpadded rows with XOR-swizzled 16-byte chunks, so a tile is
@@ -264,6 +270,92 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, i
   return alpha;
 }
 
+// P = exp2(S c + neg_m) for one tile, rounded to bf16 for the MFMA; returns
+// this lane's share of the tile's row sum, taken over the fp32 P (the
+// logsumexp needs the unrounded weights).
+__device__ __forceinline__ float exp_tile(const f32x16 (&s)[kBC / 32], float c_log2, float neg_m,
+                                          bf16x8 (&pf)[kBC / 16]) {
+  float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, neg_m));
+      l4[r & 3] += p;
+      pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
+    }
+  return (l4[0] + l4[1]) + (l4[2] + l4[3]);
+}
+
+// Online softmax of one tile against the current reference maximum, without
+// a row maximum (the d = 64 path): any reference gives the same acc / l, so
+// the reference is only moved when keeping it would let P grow past kPMax.  The lane's tile
+// sum bounds every P it holds, so one compare per lane detects that (and
+// catches the first tile, where the reference is -inf and P is inf or NaN).
+// Returns whether some lane of the wave must redo the tile with a new
+// reference (softmax_redo); *lt receives this lane's tile sum.
+template <bool MASKED>
+__device__ __forceinline__ bool softmax_tile_lagged(f32x16 (&s)[kBC / 32], int key0, int lim, int h, float c_log2,
+                                             float m_ref, bf16x8 (&pf)[kBC / 16], float* lt) {
+  constexpr int kKb = kBC / 32;
+  if (MASKED) {
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+        if (key > lim) s[kb][r] = -INFINITY;
+      }
+  }
+  float sum = exp_tile(s, c_log2, -m_ref, pf);
+  // Materialise P and the sum here: without these empty asm uses the
+  // compiler sinks the exponentials into the next step, next to the MFMAs
+  // that consume them, where they would no longer overlap this step's MFMAs.
+#pragma unroll
+  for (int t = 0; t < kBC / 16; ++t) asm volatile("" : "+v"(pf[t]));
+  asm volatile("" : "+v"(sum));
+  *lt = sum;
+  return __builtin_amdgcn_ballot_w64(!(sum <= kPMax)) != 0;
+}
+
+// The rare path of softmax_tile: the row maximum of the (masked) tile, the
+// reference moved up to it where it is larger, and P recomputed.  Returns
+// alpha = exp2(m_old - m_new), the factor for the running sum and the
+// accumulators (0 on the first tile, 1 where the reference stays).
+template <int D>
+__device__ __forceinline__ float softmax_redo(const f32x16 (&s)[kBC / 32], float c_log2, RowState<D>& st,
+                                              bf16x8 (&pf)[kBC / 16], float* lt) {
+  constexpr int kKb = kBC / 32;
+  // row max: a three-way tree over this lane's 16 kKb scores, then the other
+  // half's.  The IEEE maximum (NaN-propagating) maps to v_maximum3_f32 and,
+  // unlike fmaxf, needs no canonicalising moves of the MFMA results.
+  float part[16 * kKb];
+#pragma unroll
+  for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[kb * 16 + r] = s[kb][r];
+  int n = 16 * kKb;
+#pragma unroll
+  for (int round = 0; round < 6; ++round) {
+    if (n <= 1) break;
+    const int m = (n + 2) / 3;
+#pragma unroll
+    for (int r = 0; r < m; ++r) {
+      const float a = part[3 * r];
+      const float b = 3 * r + 1 < n ? part[3 * r + 1] : a;
+      const float c = 3 * r + 2 < n ? part[3 * r + 2] : a;
+      part[r] = __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+    }
+    n = m;
+  }
+  const float m_tile = max_halves(part[0]) * c_log2;
+  const float m_new = fmaxf(st.m_ref, m_tile);
+  const float alpha = (m_new == st.m_ref) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
+  st.m_ref = m_new;
+  *lt = exp_tile(s, c_log2, (m_new == -INFINITY) ? 0.f : -m_new, pf);
+  return alpha;
+}
+
 // Everything a pipeline step needs besides the running state.
 template <int D>
 struct Ctx {
@@ -343,8 +435,13 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
     mfma(i);
     if (i % kCopyEvery == 1) copy(i / kCopyEvery);
   }
-  bool rescale;
-  const float alpha = softmax_tile<D, MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st, p_out, &rescale);
+  // d = 64: the lagged reference without a row maximum (about 5% faster
+  // there; no gain for d = 128, whose MFMA work per tile hides the max tree)
+  constexpr bool kNoMax = (D == 64);
+  bool rescale = false;
+  float alpha = 1.f, lt = 0.f;
+  if constexpr (kNoMax) rescale = softmax_tile_lagged<MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st.m_ref, p_out, &lt);
+  else alpha = softmax_tile<D, MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st, p_out, &rescale);
   // Interleave: each step pair is two MFMAs, its operand reads and an equal
   // share of the softmax's VALU work between and after them (mask 0x008
   // MFMA, 0x100 LDS read, 0x002 VALU, 0x010 VMEM).
@@ -358,7 +455,17 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
     if (i % kCopyEvery == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
   }
-  if (rescale) {
+  if constexpr (kNoMax) {
+    if (rescale) {
+      alpha = softmax_redo<D>(s_in, c.c_log2, st, p_out, &lt);
+      st.l_part *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[ct][r] *= alpha;
+    }
+    st.l_part += lt;
+  } else if (rescale) {
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll

@@ -10,10 +10,17 @@ Sources cited in this package (pages on IO-aware exact attention):
        (answer.freetools.me)
   [P3] "GPU Kernel 入门：Triton / FlashAttention" (ai.clawlihai.cn)
 
-Pinned by the CPU tests (tests/test_oracle_pins.py, tests/test_oracle_bwd_pins.py):
+The FP8 forward (oracle/fp8.py: the E4M3 format, per-head quantisation with
+incoherent processing, attention with P rounded to E4M3) is imported as
+`oracle.fp8`.
+
+Pinned by the CPU tests (tests/test_oracle_pins.py, tests/test_oracle_bwd_pins.py,
+tests/test_oracle_fp8_pins.py):
 the printed worked example of [P3] 动手, brute-force scalar evaluation, an
 independent library softmax and autograd, central finite differences of the
-forward, closed forms, invariants.  No function here is "parity unpinned".
+forward, closed forms, invariants; for FP8 the format's definition, an
+exhaustive nearest-value search, Hadamard algebra, exact scaling identities
+and a hand-computed example.  No function here is "parity unpinned".
 """
 from .attention import (softmax_rows, online_softmax_rows, attention_head_rows,
                         attention, attention_rows, probs_head)

@@ -12,6 +12,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 --splitkv S measures fa_fwd_splitkv with S key ranges per query block (-1:
 the library's plan) instead of fa_fwd.
 --fa1order measures the K/V-outer loop-order ablation fa_fwd_fa1order.
+--fp8 measures the FP8 forward fa_fwd_fp8 on E4M3 operands that fa_quant_fp8
+made beforehand (Q and K with the Hadamard rotation), against the FP8 dense
+MFMA peak; the quantisation pass is timed separately and reported beside it.
 --bwd measures fa_bwd (dQ, dK, dV from the forward's O and LSE; the three
 kernels of one call) instead of the forward, against 2.5x the forward FLOPs.
 --all also times every named workload, forward and backward, and a non-causal N=16384, d=128 run
@@ -34,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOPS & % of MI355X bf16 MFMA peak at N=16K,d=128 (1 GPU)"
 METRIC_BWD = "attention bwd TFLOPS (5 products, 2.5x fwd FLOPs) & % of MI355X bf16 MFMA peak (1 GPU)"
+METRIC_FP8 = "attention fwd FP8 (E4M3) TFLOPS & % of MI355X fp8 MFMA peak at N=16K,d=128 (1 GPU)"
 
 KERNEL_SOURCE = os.path.join(ROOT, "io_aware_exact_13_amd", "csrc", "fa_fwd.hip")
 
@@ -89,7 +93,7 @@ def log_sclk(when):
         log(f"[bench] sclk {when}: unreadable ({e.strerror})")
 
 
-def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False):
+def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, fp8=False):
     """Time `steps` calls of the forward (or, with backward, of fa_bwd on the
     forward's outputs) with HIP events on the launch stream: returns the total
     of the timed region and the sorted per-call durations, in ms."""
@@ -119,6 +123,14 @@ def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False):
         def call():
             fa.fwd_fa1order(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, o_acc=o_acc, m=m_ws, l=l_ws,
                             stream=stream)
+    elif fp8:
+        signs = workloads.make_fp8_signs(w.seed, w.d)
+        q8, qd = fa.quant_fp8(q, rotate=True, sign_bits=signs)
+        k8, kd = fa.quant_fp8(k, rotate=True, sign_bits=signs)
+        v8, vd = fa.quant_fp8(v, rotate=False)
+
+        def call():
+            fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
     elif n_splits:
         o_part = torch.empty((n_splits, w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
         lse_part = torch.empty((n_splits, w.B, w.H, w.N), dtype=torch.float32, device=dev)
@@ -149,18 +161,67 @@ def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False):
     return total_ms, per
 
 
+def time_quant_fp8(w, steps, warmup):
+    """Average time of one fa_quant_fp8 call (rotated) on the workload's Q, in ms,
+    and its algorithmic bytes (bf16 read twice, E4M3 written once)."""
+    import torch
+    import io_aware_exact_13_amd as fa
+    import workloads
+    dev = torch.device("cuda:0")
+    q = workloads.make_inputs(w)[0].to(dev)
+    x8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+    desc = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    signs = workloads.make_fp8_signs(w.seed, w.d)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        fa.quant_fp8(q, rotate=True, sign_bits=signs, out=x8, descale=desc, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        fa.quant_fp8(q, rotate=True, sign_bits=signs, out=x8, descale=desc, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps, 5 * q.numel()
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                   default=os.cpu_count())
+    except Exception:  # noqa: BLE001
+        return os.cpu_count()
+
+
+def cpu_baseline_fp8(w):
+    """Time the oracle's FP8 forward (quantisation of one head's Q, K, V, then
+    the online softmax with P rounded to E4M3) on one whole head."""
+    import numpy as np
+    from oracle import fp8 as ofp8
+    import workloads
+    q, k, v = workloads.make_inputs(w)
+    signs = workloads.make_fp8_signs(w.seed, w.d)
+    t0 = time.perf_counter()
+    cq, _, dq = ofp8.quantize_heads(q[:1, :1].float().numpy(), True, signs)
+    ck, _, dk = ofp8.quantize_heads(k[:1, :1].float().numpy(), True, signs)
+    cv, _, dv = ofp8.quantize_heads(v[:1, :1].float().numpy(), False, 0)
+    deq = [ofp8.dequantize_heads(c, s) for c, s in ((cq, dq), (ck, dk), (cv, dv))]
+    ofp8.attention_fp8(*deq, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"1 of {w.B * w.H} heads of {w.name} (all {w.N} query rows), FP8 oracle "
+                      f"(quantisation + online softmax with E4M3 P, fp64 numpy), {dt:.1f} s"}
+
+
 def cpu_baseline(w, n_heads=32, backward=False):
     """Time the oracle on `n_heads` whole heads of the workload (every query
     row): the forward, or with backward the gradients."""
     import numpy as np
     import oracle
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"), default=os.cpu_count())
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count()
+    threads = blas_threads()
     n_heads = min(n_heads, w.B * w.H)
     q, k, v = workloads.make_inputs(w)
     do = workloads.make_grad(w) if backward else None
@@ -193,6 +254,7 @@ def main():
                     help="measure the K/V-outer loop order ablation (fa_fwd_fa1order) instead of fa_fwd")
     ap.add_argument("--splitkv", type=int, default=0,
                     help="measure fa_fwd_splitkv with this many key ranges (-1: the library's plan)")
+    ap.add_argument("--fp8", action="store_true", help="measure the FP8 forward fa_fwd_fp8 instead of fa_fwd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 3 times (counter calibration)")
     args = ap.parse_args()
@@ -232,27 +294,37 @@ def main():
     if args.splitkv < 0:
         args.splitkv = fa.fa_fwd_splitkv_plan(w.B, w.H, w.N, w.d, int(w.causal))[0]
     total_ms, per = time_workload(w, args.steps, args.warmup, backward=args.bwd,
-                                  n_splits=0 if args.bwd else args.splitkv, fa1order=args.fa1order)
+                                  n_splits=0 if args.bwd else args.splitkv, fa1order=args.fa1order, fp8=args.fp8)
     log_sclk("after")
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = acc.PEAK_FP8_DENSE_TFLOPS if args.fp8 else acc.PEAK_BF16_DENSE_TFLOPS
     rows, keys, waves, blocks = fa.fa_fwd_tile(w.B, w.H, w.N, w.d, int(w.causal))
     log(f"[bench] {ms_step:.4f} ms/step, median launch {per[len(per) // 2]:.4f} ms, "
-        f"min {per[0]:.4f} ms -> {value:.1f} TFLOP/s ({100 * value / acc.PEAK_BF16_DENSE_TFLOPS:.1f}% of peak)")
+        f"min {per[0]:.4f} ms -> {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak)")
+    quant = None
+    if args.fp8:
+        qms, qbytes = time_quant_fp8(w, max(5, args.steps // 2), 3)
+        quant = {"ms_per_tensor": round(qms, 5), "GB/s": round(qbytes / (qms * 1e-3) / 1e9, 1),
+                 "bytes": qbytes}
+        log(f"[bench] fa_quant_fp8 (rotated) {qms * 1e3:.1f} us per tensor, {quant['GB/s']} GB/s "
+            f"(bf16 read twice + E4M3 written)")
 
     if args.all:
         extra = workloads.custom(1, 32, 16384, 128, False, seed=3)
         for ow in [workloads.WORKLOADS[o] for o in workloads.WORKLOAD_ORDER] + [extra]:
             other = ow.name
-            for bw in (False, True):
-                tms, p = time_workload(ow, max(5, args.steps // 2), 3, backward=bw)
+            for mode in ("fwd", "bwd", "fp8"):
+                bw = mode == "bwd"
+                tms, p = time_workload(ow, max(5, args.steps // 2), 3, backward=bw, fp8=mode == "fp8")
                 f = (acc.attention_bwd_flops if bw else acc.attention_flops)(ow.B, ow.H, ow.N, ow.d, ow.causal)
                 t = tms / max(5, args.steps // 2)
-                log(f"[bench-all] {other:32s} {'bwd' if bw else 'fwd'} {t * 1e3:9.1f} us  "
+                pk = acc.PEAK_FP8_DENSE_TFLOPS if mode == "fp8" else acc.PEAK_BF16_DENSE_TFLOPS
+                log(f"[bench-all] {other:32s} {mode} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s "
-                    f"{100 * f / (t * 1e-3) / 1e12 / acc.PEAK_BF16_DENSE_TFLOPS:5.1f}%")
+                    f"{100 * f / (t * 1e-3) / 1e12 / pk:5.1f}% of its peak")
         # split-KV forward where the query blocks under-fill the GPU: one GPU's
         # share of the 16K causal workload over 8 GPUs (4 heads) and the tiny one
         for sw in (workloads.custom(1, 4, 16384, 128, True, seed=3), workloads.WORKLOADS["tiny_b1h1_n256_d64"]):
@@ -264,9 +336,9 @@ def main():
                 log(f"[bench-all] {sw.name:32s} {'fwd' if ns == 0 else f'split{ns}':>7s} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s{'  (plan)' if ns == plan else ''}")
 
-    traffic = None if (args.bwd or args.splitkv or args.fa1order) else measured_traffic(name)
+    traffic = None if (args.bwd or args.splitkv or args.fa1order or args.fp8) else measured_traffic(name)
     result = {
-        "metric": METRIC_BWD if args.bwd else METRIC,
+        "metric": METRIC_BWD if args.bwd else (METRIC_FP8 if args.fp8 else METRIC),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -276,23 +348,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": name,
-                   "pass": "bwd" if args.bwd else ("fwd_fa1order" if args.fa1order else
+                   "pass": "bwd" if args.bwd else ("fwd_fa1order" if args.fa1order else "fwd_fp8" if args.fp8 else
                                                    (f"fwd_splitkv{args.splitkv}" if args.splitkv else "fwd")), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "seed": w.seed,
                    "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
+                   **({"pct_of_fp8_peak": round(100 * value / peak, 2), "quantisation": quant} if args.fp8 else {}),
                    "launch": {"rows_per_block": rows, "keys_per_tile": keys, "waves": waves,
                               "blocks": blocks}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": acc.PEAK_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / acc.PEAK_BF16_DENSE_TFLOPS, 4),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
                      "traffic": traffic},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(w, n_heads=8 if args.bwd else 32, backward=args.bwd)
+        result["cpu_baseline"] = (cpu_baseline_fp8(w) if args.fp8 else
+                                  cpu_baseline(w, n_heads=8 if args.bwd else 32, backward=args.bwd))
     print(json.dumps(result), flush=True)
 
 

@@ -26,6 +26,7 @@
 #define FA_MI355X_H
 
 #include <hip/hip_runtime_api.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -175,6 +176,68 @@ int fa_fwd_fa1order(const void* q, const void* k, const void* v, void* o, float*
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * FP8 forward.  Source: "为什么Flash Attention能将注意力计算提速数倍而不损失精度",
+ * section Flash Attention 3 (FP8 low-precision support): the forward on the
+ * FP8 matrix units, with incoherent processing to lower the quantisation
+ * error.  The page fixes no scheme; these two calls implement this one:
+ *   format     OCP FP8 E4M3 (bias 7, largest finite 448, NaN = S.1111.111),
+ *              round to nearest even;
+ *   scaling    one factor per (batch, head) and tensor: amax = max |y| over
+ *              the head, code = E4M3(y * 448 / amax), descale = amax / 448;
+ *   rotation   optional for Q and K: y = (sigma o x) H with sigma a random
+ *              sign diagonal and H the Sylvester-Hadamard matrix (+-1
+ *              entries), computed by the fast Walsh-Hadamard butterfly in
+ *              fp32; descale then also carries 1/sqrt(d), so the dequantised
+ *              rows are the orthonormally rotated ones and Q K^T is kept.
+ *   attention  the online softmax of fa_fwd with P, taken against the
+ *              running row maximum (P <= 1), rounded to E4M3 before P V; the
+ *              running sum adds the unrounded P.
+ */
+
+/*
+ * fa_quant_fp8 -- quantise a bf16 [B][H][N][d] tensor to E4M3 per head.
+ *
+ *   x         bf16 input, [B][H][N][d] contiguous, 16-byte aligned.  Read
+ *             only.  Values must be finite.
+ *   x8        E4M3 codes, same layout (one byte per element), 8-byte
+ *             aligned; fully overwritten.
+ *   descale   fp32 [B][H], 4-byte aligned; overwritten with each head's
+ *             dequantisation factor (0 for an all-zero head, whose codes are
+ *             0).  During the call it holds the heads' amax.
+ *   B, H, N, d  as for fa_fwd (d = 64 or 128).
+ *   rotate    0: y = x; 1: the random-sign Hadamard rotation above (use the
+ *             same signs for Q and K, and no rotation for V).
+ *   sign_lo, sign_hi  the 128-bit sign mask: sigma_c = -1 where bit c is set
+ *             (bit c of sign_lo for c < 64, bit c - 64 of sign_hi otherwise;
+ *             bits at or past d are ignored).
+ *   stream    HIP stream.
+ * Four kernels run in order on `stream` (clear, amax, quantise, descale);
+ * codes and factors are bitwise reproducible.  Returns FA_OK or FA_ERR_NULL,
+ * _SHAPE, _HEAD_DIM, _FLAG (rotate not 0/1), _ALIGN, _ALIAS, _LAUNCH.
+ */
+int fa_quant_fp8(const void* x, void* x8, float* descale, int B, int H, int N, int d, int rotate,
+                 uint64_t sign_lo, uint64_t sign_hi, hipStream_t stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward on E4M3 operands (as fa_quant_fp8 makes
+ * them), on `stream`.
+ *
+ *   q8, k8, v8  E4M3 [B][H][N][d], 16-byte aligned.  Read only.
+ *   q_descale, k_descale, v_descale  fp32 [B][H] factors, 4-byte aligned:
+ *             the operands are descale * value(code).
+ *   o         bf16 [B][H][N][d], 16-byte aligned; fully overwritten.
+ *   lse       fp32 [B][H][N], 4-byte aligned; natural-log logsumexp of the
+ *             scaled, masked scores of the dequantised operands.
+ *   B, H, N, d, scale, causal  as for fa_fwd.
+ * Same host checks and asynchrony as fa_fwd; outputs must not overlap the
+ * inputs or each other; nothing is allocated; results are bitwise
+ * reproducible run to run.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale,
+               const float* k_descale, const float* v_descale, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 #ifdef __cplusplus
 }

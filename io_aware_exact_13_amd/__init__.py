@@ -60,6 +60,11 @@ def load_library():
     lib.fa_fwd_splitkv_plan.restype = ci
     lib.fa_fwd_fa1order.argtypes = [vp] * 5 + [ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, vp, vp]
     lib.fa_fwd_fa1order.restype = ci
+    u64 = ctypes.c_uint64
+    lib.fa_quant_fp8.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, u64, u64, vp]
+    lib.fa_quant_fp8.restype = ci
+    lib.fa_fwd_fp8.argtypes = [vp] * 8 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    lib.fa_fwd_fp8.restype = ci
     _lib = lib
     return lib
 
@@ -97,6 +102,18 @@ def fa_fwd_fa1order(q, k, v, o, lse, B, H, N, d, scale, causal, o_acc, m, l, str
     """C-ABI fa_fwd_fa1order with raw device addresses (ints); returns the status code."""
     return load_library().fa_fwd_fa1order(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), int(causal),
                                           o_acc, m, l, stream)
+
+
+def fa_quant_fp8(x, x8, descale, B, H, N, d, rotate, sign_lo, sign_hi, stream) -> int:
+    """C-ABI fa_quant_fp8 with raw device addresses (ints); returns the status code."""
+    return load_library().fa_quant_fp8(x, x8, descale, B, H, N, d, int(rotate), ctypes.c_uint64(sign_lo),
+                                       ctypes.c_uint64(sign_hi), stream)
+
+
+def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, B, H, N, d, scale, causal, stream) -> int:
+    """C-ABI fa_fwd_fp8 with raw device addresses (ints); returns the status code."""
+    return load_library().fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, B, H, N, d,
+                                     ctypes.c_float(scale), int(causal), stream)
 
 
 def fa_status_str(status: int) -> str:
@@ -248,4 +265,56 @@ def fwd_fa1order(q, k, v, scale=None, causal=False, out=None, lse=None, o_acc=No
                          stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_fa1order")
+    return out, lse
+
+
+def quant_fp8(x, rotate=False, sign_bits=0, out=None, descale=None, stream=None):
+    """Per-head E4M3 quantisation of a bf16 [B, H, N, d] tensor: returns
+    (codes uint8 [B, H, N, d], descale fp32 [B, H]).  With `rotate`, rows get
+    the random-sign Hadamard rotation whose signs are the bits of the
+    128-bit integer `sign_bits` (bit c set: channel c negated)."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 GPU tensor [B, H, N, d]")
+    B, H, N, d = x.shape
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    descale = torch.empty((B, H), dtype=torch.float32, device=x.device) if descale is None else descale
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    bits = int(sign_bits)
+    st = fa_quant_fp8(x.data_ptr(), out.data_ptr(), descale.data_ptr(), B, H, N, d, int(bool(rotate)),
+                      bits & 0xFFFFFFFFFFFFFFFF, (bits >> 64) & 0xFFFFFFFFFFFFFFFF, stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_quant_fp8")
+    return out, descale
+
+
+def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, scale=None, causal=False, out=None, lse=None,
+            stream=None):
+    """Attention forward on E4M3 operands (uint8 or float8_e4m3fn [B, H, N, d])
+    with fp32 [B, H] dequantisation factors: returns (o bf16, lse fp32)."""
+    import torch
+    t8 = [t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t for t in (q8, k8, v8)]
+    if any(t.dtype != torch.uint8 for t in t8):
+        raise TypeError("q8, k8, v8 must be uint8 or float8_e4m3fn")
+    q8, k8, v8 = t8
+    if q8.dim() != 4 or q8.shape != k8.shape or q8.shape != v8.shape:
+        raise ValueError("q8, k8, v8 must share one [B, H, N, d] shape")
+    if not (q8.is_contiguous() and k8.is_contiguous() and v8.is_contiguous()):
+        raise ValueError("q8, k8, v8 must be contiguous")
+    B, H, N, d = q8.shape
+    for t in (q_descale, k_descale, v_descale):
+        if t.dtype != torch.float32 or t.numel() != B * H or not t.is_contiguous():
+            raise ValueError("descale factors must be contiguous fp32 [B, H]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device)
+    st = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
+                    v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                    int(bool(causal)), stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
     return out, lse

@@ -17,6 +17,7 @@ MIB = 1 << 20
 
 # MI355X published peaks used as roofline denominators.
 PEAK_BF16_DENSE_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz
+PEAK_FP8_DENSE_TFLOPS = 5033.2      # twice the bf16 rate (E4M3 / E5M2 MFMA)
 PEAK_HBM_GBPS = 8000.0
 
 

@@ -99,3 +99,27 @@ def sample_picks(w: workloads.Workload, n_heads=3, n_rand=48, seed=0):
                 rows.add(edge)
         picks.append((b, h, np.array(sorted(rows))))
     return picks
+
+
+def fp8_flip_allowance(q, k, v, scale, causal, rows):
+    """Per element of the given rows of one head (dequantised fp64 operands):
+    how far O_ic moves when one E4M3 rounding of P lands on the other side of
+    a midpoint, which fp32 (GPU) and fp64 (oracle) evaluations of P may do
+    when P lies within rounding noise of it.  One code step is at most 2^-3
+    of a normal P and 2^-9 in the subnormal range; a term's P is its final
+    softmax weight w_ij times l_i e^{m_t - m_i} <= l_i, so the move is at most
+    2^-3 max_j w_ij |v_jc| + 2^-9 max_j |v_jc| / l_i
+    (l_i = sum_j e^{s_ij - m_i} over the visible keys)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    n = k.shape[0]
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] > rows[:, None], -np.inf, s)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    l = e.sum(axis=1, keepdims=True)
+    w = e / l
+    av = np.abs(v)
+    top = np.zeros((rows.size, v.shape[1]))
+    for c0 in range(0, n, 512):
+        top = np.maximum(top, (w[:, c0:c0 + 512, None] * av[None, c0:c0 + 512, :]).max(axis=1))
+    return 2.0 ** -3 * top + 2.0 ** -9 * av.max(axis=0)[None, :] / l

@@ -25,8 +25,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_fa1order", "fa_fwd_splitkv", "fa_fwd_splitkv_plan",
-                                    "fa_fwd_tile", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_fa1order", "fa_fwd_fp8", "fa_fwd_splitkv",
+                                    "fa_fwd_splitkv_plan", "fa_fwd_tile", "fa_quant_fp8", "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -158,3 +158,39 @@ def call_fa1(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=16, d=64, scale=0.125, causa
 ])
 def test_bad_fa1order_arguments_are_rejected_on_the_host(lib, kw, code):
     assert call_fa1(**kw) == code
+
+
+# fa_quant_fp8 / fa_fwd_fp8: fake addresses; every call is rejected on the host.
+X8, DS, DQ, DK, DV = 16 << 40, 17 << 40, 18 << 40, 19 << 40, 20 << 40
+
+
+def call_quant(x=Q, x8=X8, descale=DS, B=1, H=1, N=16, d=64, rotate=0):
+    return fa.fa_quant_fp8(x, x8, descale, B, H, N, d, rotate, 0x1234, 0x5678, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), fa.FA_ERR_NULL), (dict(x8=0), fa.FA_ERR_NULL), (dict(descale=0), fa.FA_ERR_NULL),
+    (dict(B=0), fa.FA_ERR_SHAPE), (dict(N=-3), fa.FA_ERR_SHAPE), (dict(B=1 << 20, H=1 << 20), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_HEAD_DIM), (dict(rotate=2), fa.FA_ERR_FLAG),
+    (dict(x=Q + 8), fa.FA_ERR_ALIGN), (dict(x8=X8 + 4), fa.FA_ERR_ALIGN), (dict(descale=DS + 2), fa.FA_ERR_ALIGN),
+    (dict(x8=Q + 512), fa.FA_ERR_ALIAS), (dict(descale=X8 + 8), fa.FA_ERR_ALIAS), (dict(descale=Q), fa.FA_ERR_ALIAS),
+])
+def test_bad_quant_fp8_arguments_are_rejected_on_the_host(lib, kw, code):
+    assert call_quant(**kw) == code
+
+
+def call_fp8(q=Q, k=K, v=V, qd=DQ, kd=DK, vd=DV, o=O, lse=L, B=1, H=1, N=16, d=64, scale=0.125, causal=0):
+    return fa.fa_fwd_fp8(q, k, v, qd, kd, vd, o, lse, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_NULL), (dict(kd=0), fa.FA_ERR_NULL), (dict(lse=0), fa.FA_ERR_NULL),
+    (dict(H=0), fa.FA_ERR_SHAPE), (dict(d=32), fa.FA_ERR_HEAD_DIM), (dict(causal=3), fa.FA_ERR_FLAG),
+    (dict(scale=float("nan")), fa.FA_ERR_SCALE), (dict(scale=0.0), fa.FA_ERR_SCALE),
+    (dict(v=V + 8), fa.FA_ERR_ALIGN), (dict(vd=DV + 1), fa.FA_ERR_ALIGN), (dict(o=O + 4), fa.FA_ERR_ALIGN),
+    (dict(o=K), fa.FA_ERR_ALIAS), (dict(lse=DQ), fa.FA_ERR_ALIAS), (dict(lse=O + 64), fa.FA_ERR_ALIAS),
+    (dict(o=V - 1024), fa.FA_ERR_ALIAS),
+])
+def test_bad_fwd_fp8_arguments_are_rejected_on_the_host(lib, kw, code):
+    assert call_fp8(**kw) == code
+

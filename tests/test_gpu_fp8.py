@@ -1,0 +1,213 @@
+"""The FP8 path (fa_quant_fp8, fa_fwd_fp8) against the oracle (GPU only).
+
+Quantisation: codes and descale factors are integers / fp32 values the
+definition fixes, so they must agree bit for bit with oracle.fp8.quantize_heads.
+
+Attention: the oracle is fed its own quantisation of the bf16 inputs (the
+GPU gets the same codes), and computes the online softmax with P rounded to
+E4M3 (oracle.fp8.attention_fp8) in fp64.  The GPU's P is fp32, so a P within
+rounding noise of a midpoint between two codes may round the other way; the
+bar per element is |dO| <= half a bf16 ulp of O + the move of one such flip
+(gpu_common.fp8_flip_allowance) + 1e-6; the mean of what |dO| exceeds half a
+bf16 ulp by (the error the bf16 output does not explain) <= 1e-4; and
+|dLSE| <= 1e-3 (the LSE adds unrounded P on both sides).
+"""
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_13_amd as fa
+import oracle
+import workloads
+from gpu_common import announce, bf16_half_ulp, device, fp8_flip_allowance, to64
+from oracle import fp8 as ofp8
+
+pytestmark = pytest.mark.gpu
+
+O_MEAN_EXCESS = 1e-4
+LSE_MAX = 1e-3
+
+
+def gpu_quant(x, rotate, signs):
+    x8, desc = fa.quant_fp8(x.to(device()), rotate=rotate, sign_bits=signs)
+    torch.cuda.synchronize()
+    return x8.cpu().numpy(), desc.cpu().numpy()
+
+
+def oracle_quant(q, k, v, rotate, signs):
+    cq, _, dq = ofp8.quantize_heads(q.float().numpy(), rotate, signs)
+    ck, _, dk = ofp8.quantize_heads(k.float().numpy(), rotate, signs)
+    cv, _, dv = ofp8.quantize_heads(v.float().numpy(), False, 0)
+    return (cq, dq), (ck, dk), (cv, dv)
+
+
+def gpu_fwd_fp8(qq, kk, vv, scale, causal):
+    dev = device()
+    t = [torch.from_numpy(np.ascontiguousarray(c)).to(dev) for c, _ in (qq, kk, vv)]
+    d = [torch.from_numpy(np.ascontiguousarray(s)).to(dev) for _, s in (qq, kk, vv)]
+    o, lse = fa.fwd_fp8(*t, *d, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_rows(qq, kk, vv, scale, causal, o, lse, picks):
+    """Compare the GPU's O/LSE on (b, h, rows) picks with the oracle; returns
+    (max excess over the per-element bar, mean excess of |dO| over half a
+    bf16 ulp, max |dLSE|)."""
+    worst, worst_l, tot, cnt = -np.inf, 0.0, 0.0, 0
+    deq = [ofp8.dequantize_heads(c, s) for c, s in (qq, kk, vv)]
+    for b, h, rows in picks:
+        qd, kd, vd = (x[b, h] for x in deq)
+        ro, rl = ofp8.attention_fp8_head_rows(qd, kd, vd, scale, causal, rows)
+        go = to64(o[b, h, torch.as_tensor(rows)])
+        gl = to64(lse[b, h, torch.as_tensor(rows)])
+        diff = np.abs(go - ro)
+        half = bf16_half_ulp(ro)
+        bar = half + fp8_flip_allowance(qd, kd, vd, scale, causal, rows) + 1e-6
+        worst = max(worst, float((diff - bar).max()))
+        worst_l = max(worst_l, float(np.abs(gl - rl).max()))
+        tot += float(np.maximum(diff - half, 0.0).sum())
+        cnt += diff.size
+    return worst, tot / cnt, worst_l
+
+
+QUANT_CASES = [(1, 1, 1, 64), (1, 2, 333, 128), (2, 3, 100, 64), (1, 2, 4096, 128), (1, 1, 700, 64)]
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("B,H,N,d", QUANT_CASES)
+def test_quantisation_is_bit_exact(B, H, N, d, rotate):
+    w = workloads.custom(B, H, N, d, False, seed=6000 + N + d)
+    q, k, v = workloads.make_inputs(w)
+    q[0, 0] = 0                                    # an all-zero head: codes 0, descale 0
+    signs = workloads.make_fp8_signs(w.seed, d)
+    announce(f"[fp8-quant] {w.name} rotate={rotate}")
+    for x in (q, k):
+        g8, gd = gpu_quant(x, rotate, signs)
+        c, _, ds = ofp8.quantize_heads(x.float().numpy(), rotate, signs)
+        assert np.array_equal(g8, c), int((g8 != c).sum())
+        assert np.array_equal(gd.view(np.uint32), ds.view(np.uint32))
+        if x is q:                                 # zeros (the rotation may give -0, code 0x80)
+            assert not (g8[0, 0] & 0x7F).any() and gd[0, 0] == 0
+
+
+def test_quantisation_of_peaky_and_outlier_inputs_is_bit_exact():
+    for w, maker in ((workloads.custom(1, 2, 2048, 128, True, seed=6101, peaky=True), workloads.make_inputs),
+                     (workloads.custom(1, 2, 1024, 128, True, seed=6102), workloads.make_outlier_inputs),
+                     (workloads.custom(2, 1, 513, 64, True, seed=6103), workloads.make_outlier_inputs)):
+        q, k, v = maker(w)
+        signs = workloads.make_fp8_signs(w.seed, w.d)
+        for rotate in (False, True):
+            for x in (q, k, v):
+                g8, gd = gpu_quant(x, rotate, signs)
+                c, _, ds = ofp8.quantize_heads(x.float().numpy(), rotate, signs)
+                assert np.array_equal(g8, c) and np.array_equal(gd.view(np.uint32), ds.view(np.uint32))
+
+
+ATT_CASES = [
+    (1, 1, 256, 64, False), (1, 2, 333, 128, False), (2, 1, 1000, 64, True), (1, 3, 700, 128, True),
+    (1, 1, 1, 128, False), (1, 1, 65, 64, True), (1, 2, 513, 128, True), (1, 1, 4096, 128, True),
+    (1, 1, 2048, 64, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", ATT_CASES)
+def test_fp8_attention_matches_oracle(B, H, N, d, causal):
+    w = workloads.custom(B, H, N, d, causal, seed=6200 + N + d + int(causal))
+    q, k, v = workloads.make_inputs(w)
+    rotate = d == 128
+    qq, kk, vv = oracle_quant(q, k, v, rotate, workloads.make_fp8_signs(w.seed, d))
+    announce(f"[fp8-att] {w.name} rotate={rotate}")
+    o, lse = gpu_fwd_fp8(qq, kk, vv, w.scale, causal)
+    picks = [(b, h, np.arange(N)) for b in range(B) for h in range(H)]
+    worst, mean, dl = check_rows(qq, kk, vv, w.scale, causal, o, lse, picks)
+    announce(f"    excess over bar {worst:.3e}  mean excess {mean:.3e}  max|dLSE| {dl:.3e}")
+    assert worst <= 0 and mean <= O_MEAN_EXCESS and dl <= LSE_MAX
+
+
+def test_fp8_headline_shape_on_sampled_rows():
+    """1 x 32 x 16384 x 128, causal: the GPU quantises all heads (two checked
+    bit for bit against the oracle), the GPU forward runs on its codes, and
+    sampled rows of those two heads are checked against the oracle run on the
+    oracle's own codes."""
+    dev = device()
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    q, k, v = workloads.make_inputs(w)
+    signs = workloads.make_fp8_signs(w.seed, w.d)
+    announce("[fp8-headline] quantising")
+    q8, qd = fa.quant_fp8(q.to(dev), rotate=True, sign_bits=signs)
+    k8, kd = fa.quant_fp8(k.to(dev), rotate=True, sign_bits=signs)
+    v8, vd = fa.quant_fp8(v.to(dev), rotate=False)
+    o, lse = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(17)
+    for h in (0, 31):
+        announce(f"[fp8-headline] head {h}: oracle quantisation and rows")
+        qq, kk, vv = oracle_quant(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], True, signs)
+        for (c, s), (g8, gs) in zip((qq, kk, vv), ((q8, qd), (k8, kd), (v8, vd))):
+            assert np.array_equal(g8[:, h:h + 1].cpu().numpy(), c)
+            assert np.array_equal(gs[:, h:h + 1].cpu().numpy().view(np.uint32), s.view(np.uint32))
+        rows = np.array(sorted(set(range(40)) | set(range(w.N - 40, w.N)) |
+                               set(rng.integers(0, w.N, 48).tolist()) | {255, 256, 8191, 8192}))
+        worst, mean, dl = check_rows(qq, kk, vv, w.scale, True, o[:, h:h + 1], lse[:, h:h + 1], [(0, 0, rows)])
+        announce(f"    excess over bar {worst:.3e}  mean excess {mean:.3e}  max|dLSE| {dl:.3e}")
+        assert worst <= 0 and mean <= O_MEAN_EXCESS and dl <= LSE_MAX
+
+
+def test_fp8_special_cases():
+    """A zero V head gives O = 0 exactly; a key equal to 10 x a query row
+    dominates that row, whose O is then (up to the bf16 output) that key's
+    dequantised V row; equal keys give the mean of V."""
+    w = workloads.custom(1, 2, 300, 128, False, seed=6301)
+    q, k, v = workloads.make_inputs(w)
+    v[0, 1] = 0
+    k[0, 0, 123] = (q[0, 0, 200].float() * 10).to(torch.bfloat16)
+    qq, kk, vv = oracle_quant(q, k, v, False, 0)
+    o, lse = gpu_fwd_fp8(qq, kk, vv, w.scale, False)
+    assert torch.all(o[0, 1] == 0) and torch.isfinite(lse).all()
+    vrow = ofp8.dequantize_heads(*vv)[0, 0, 123]
+    got = to64(o[0, 0, 200])
+    assert np.all(np.abs(got - vrow) <= bf16_half_ulp(vrow) + 1e-6)
+    # all keys equal: every P is 1, O is the mean of the V rows
+    k2 = k.clone()
+    k2[:] = k[0, 0, 0]
+    qq, kk, vv = oracle_quant(q, k2, v, False, 0)
+    o, lse = gpu_fwd_fp8(qq, kk, vv, w.scale, False)
+    mean_v = ofp8.dequantize_heads(*vv)[0, 0].mean(axis=0)
+    assert np.all(np.abs(to64(o[0, 0]) - mean_v) <= bf16_half_ulp(mean_v) + 1e-5)
+
+
+def test_fp8_is_bitwise_deterministic():
+    w = workloads.custom(1, 2, 900, 128, True, seed=6401)
+    q, k, v = workloads.make_inputs(w)
+    signs = workloads.make_fp8_signs(w.seed)
+    a = [gpu_quant(x, True, signs) for x in (q, k)]
+    b = [gpu_quant(x, True, signs) for x in (q, k)]
+    for (x8, xd), (y8, yd) in zip(a, b):
+        assert np.array_equal(x8, y8) and np.array_equal(xd, yd)
+    qq, kk, vv = oracle_quant(q, k, v, True, signs)
+    o1, l1 = gpu_fwd_fp8(qq, kk, vv, w.scale, True)
+    o2, l2 = gpu_fwd_fp8(qq, kk, vv, w.scale, True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_rotation_lowers_the_fp8_error_end_to_end():
+    """Whole GPU path (quantise + forward) against the fp64 attention of the
+    bf16 inputs, on inputs with two outlier channels shared by Q and K: the
+    rotated path's error is well below the unrotated one's."""
+    dev = device()
+    w = workloads.custom(1, 4, 2048, 128, True, seed=6501)
+    q, k, v = workloads.make_outlier_inputs(w)
+    signs = workloads.make_fp8_signs(w.seed)
+    ref, _ = oracle.attention(to64(q), to64(k), to64(v), w.scale, True)
+    errs = {}
+    for rotate in (False, True):
+        q8, qd = fa.quant_fp8(q.to(dev), rotate=rotate, sign_bits=signs)
+        k8, kd = fa.quant_fp8(k.to(dev), rotate=rotate, sign_bits=signs)
+        v8, vd = fa.quant_fp8(v.to(dev), rotate=False)
+        o, _ = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=True)
+        torch.cuda.synchronize()
+        errs[rotate] = float(np.sqrt(np.mean((to64(o) - ref) ** 2)) / np.sqrt(np.mean(ref ** 2)))
+    announce(f"[fp8-outliers] relative rms error: plain {errs[False]:.3e}  rotated {errs[True]:.3e}")
+    assert errs[True] * 1.5 < errs[False]

@@ -111,3 +111,32 @@ def make_grad(w: Workload, seed: int | None = None):
     x = torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32)
     return x.to(torch.bfloat16).contiguous()
 
+
+
+FP8_SIGN_SEED_OFFSET = 104729
+OUTLIER_CHANNELS = (5, 77)
+OUTLIER_FACTOR = 16.0
+
+
+def make_fp8_signs(seed: int, d: int = 128) -> int:
+    """The random sign mask of the FP8 path's Hadamard rotation, as an integer
+    of d bits (bit c set: channel c negated), drawn from its own CPU generator
+    seeded with seed + 104729."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + FP8_SIGN_SEED_OFFSET)
+    bits = torch.randint(0, 2, (d,), generator=g).tolist()
+    return sum(int(b) << c for c, b in enumerate(bits))
+
+
+def make_outlier_inputs(w: Workload, seed: int | None = None):
+    """(q, k, v) as make_inputs, then in Q and K the channels OUTLIER_CHANNELS
+    (those below d) multiplied by OUTLIER_FACTOR (a power of two, so no bf16
+    bits change besides the exponent): a few large channels shared by Q and
+    K, the situation the FP8 path's rotation is meant for."""
+    q, k, v = make_inputs(w, seed)
+    ch = [c for c in OUTLIER_CHANNELS if c < w.d]
+    q = q.clone()
+    k = k.clone()
+    q[..., ch] *= OUTLIER_FACTOR
+    k[..., ch] *= OUTLIER_FACTOR
+    return q.contiguous(), k.contiguous(), v

@@ -301,7 +301,8 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = acc.PEAK_FP8_DENSE_TFLOPS if args.fp8 else acc.PEAK_BF16_DENSE_TFLOPS
-    rows, keys, waves, blocks = fa.fa_fwd_tile(w.B, w.H, w.N, w.d, int(w.causal))
+    tile_fn = fa.fa_fwd_fp8_tile if args.fp8 else fa.fa_fwd_tile
+    rows, keys, waves, blocks = tile_fn(w.B, w.H, w.N, w.d, int(w.causal))
     log(f"[bench] {ms_step:.4f} ms/step, median launch {per[len(per) // 2]:.4f} ms, "
         f"min {per[0]:.4f} ms -> {value:.1f} TFLOP/s ({100 * value / peak:.1f}% of peak)")
     quant = None

@@ -239,6 +239,15 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_de
                const float* k_descale, const float* v_descale, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
+/*
+ * fa_fwd_fp8_tile -- the launch shape fa_fwd_fp8 uses: query rows per
+ * workgroup, keys per K/V tile, waves per workgroup and the number of
+ * workgroups.  Returns FA_OK or the FA_ERR_* code fa_fwd_fp8 would return
+ * for these sizes (pointers are not checked here).  Host only.
+ */
+int fa_fwd_fp8_tile(int B, int H, int N, int d, int causal,
+                    int* rows_per_block, int* keys_per_tile, int* waves, long long* blocks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,9 @@ def load_library():
     lib.fa_quant_fp8.restype = ci
     lib.fa_fwd_fp8.argtypes = [vp] * 8 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_fwd_fp8.restype = ci
+    lib.fa_fwd_fp8_tile.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
+                                    ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_longlong)]
+    lib.fa_fwd_fp8_tile.restype = ci
     _lib = lib
     return lib
 
@@ -114,6 +117,17 @@ def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, B, H, N, d, 
     """C-ABI fa_fwd_fp8 with raw device addresses (ints); returns the status code."""
     return load_library().fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o, lse, B, H, N, d,
                                      ctypes.c_float(scale), int(causal), stream)
+
+
+def fa_fwd_fp8_tile(B, H, N, d, causal):
+    """(rows_per_block, keys_per_tile, waves, blocks) of the launch fa_fwd_fp8 makes."""
+    r, c, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    g = ctypes.c_longlong()
+    st = load_library().fa_fwd_fp8_tile(B, H, N, d, int(causal), ctypes.byref(r), ctypes.byref(c),
+                                        ctypes.byref(w), ctypes.byref(g))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8_tile")
+    return r.value, c.value, w.value, g.value
 
 
 def fa_status_str(status: int) -> str:

@@ -34,6 +34,11 @@
 //     serves both the K row reads and the transposed V reads without bank
 //     conflicts.  K and V tiles (64 keys, 8 KiB at d = 128) move HBM -> LDS
 //     by buffer_load ... lds through four-buffer rings, two steps ahead.
+//   * Workgroups of 4 waves (128 query rows, 64 KiB of LDS at d = 128), two
+//     per CU: each SIMD then runs waves of two independent workgroups, which
+//     drift apart, so one's softmax overlaps the other's MFMAs and barrier
+//     waits (7% faster than 8-wave workgroups of 256 rows, which hold both
+//     waves of a SIMD to the same barrier every tile).
 //   * The step structure, XCD-aware workgroup order and epilogue follow the
 //     bf16 forward (fa_fwd.hip): per step, S_{j+1}, O += V_{j-1} P_{j-1} and
 //     the softmax of tile j interleave in one instruction stream.
@@ -57,7 +62,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 
 constexpr int kBC = 64;           // keys per K/V tile
-constexpr int kWaves = 8;         // waves per workgroup, 32 query rows each
+constexpr int kWaves = 4;         // waves per workgroup, 32 query rows each
 constexpr int kThreads = kWaves * 64;
 constexpr int kBR = kWaves * 32;  // query rows per workgroup
 constexpr int kXcds = 8;
@@ -89,8 +94,8 @@ struct Geom8 {
   static constexpr int kTile = kBC * kRowBytes;
   static constexpr int kRing = 4;
   static constexpr int kLdsBytes = 2 * kRing * kTile;
-  static constexpr int kCopyWaves = kTile / 1024;          // waves that copy 1 KiB of each tile
-  static_assert(kCopyWaves >= 1 && kCopyWaves <= kWaves, "tile copy split");
+  static constexpr int kIssues = kTile / (kWaves * 1024);   // 1 KiB copies per wave per tile
+  static_assert(kIssues * kWaves * 1024 == kTile, "tile copy split");
   __host__ __device__ static constexpr int f(int r) {
     return D == 128 ? ((((r >> 1) & 3) << 1) | ((r >> 5) & 1)) : ((((r >> 2) & 1) << 1) | ((r >> 5) & 1));
   }
@@ -104,27 +109,33 @@ __host__ __device__ constexpr int s_key(int b, int i) {
   return 32 * ((i >> 2) & 1) + 16 * b + 8 * (i >> 4) + 4 * ((i >> 3) & 1) + (i & 3);
 }
 
-// One wave's 1 KiB share of an HBM -> LDS tile copy; the lane fetches the
-// global chunk the swizzle puts in its slot.  Rows past `n` read as zeros.
+// One wave's share of an HBM -> LDS tile copy, kIssues pieces of 1 KiB; the
+// lane fetches the global chunk the swizzle puts in its slot (the swizzle
+// depends on row bit 5, so each piece has its own offset).  Rows past `n`
+// read as zeros.
 template <int D>
 struct TileCopy8 {
-  unsigned voff;
+  unsigned voff[Geom8<D>::kIssues];
   __device__ __forceinline__ void init(int wave, int lane) {
     using G = Geom8<D>;
-    const int slot = wave * 64 + lane;
-    const int row = slot / G::kChunks, pchunk = slot % G::kChunks;
-    voff = (unsigned)(row * G::kRowBytes + ((pchunk ^ G::f(row)) << 4));
+#pragma unroll
+    for (int i = 0; i < G::kIssues; ++i) {
+      const int slot = (i * kWaves + wave) * 64 + lane;
+      const int row = slot / G::kChunks, pchunk = slot % G::kChunks;
+      voff[i] = (unsigned)(row * G::kRowBytes + ((pchunk ^ G::f(row)) << 4));
+    }
   }
   __device__ __forceinline__ void issue(const char* head, int key0, int n, char* dst, int wave) const {
     using G = Geom8<D>;
 #if defined(__HIP_DEVICE_COMPILE__)
-    if (wave < G::kCopyWaves) {
-      const int rows = max(n - key0, 0);
-      const char* base = head + (size_t)min(key0, n) * G::kRowBytes;
-      const __amdgpu_buffer_rsrc_t rsrc =
-          __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, rows * G::kRowBytes, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + wave * 1024), 16, voff, 0, 0, 0);
-    }
+    const int rows = max(n - key0, 0);
+    const char* base = head + (size_t)min(key0, n) * G::kRowBytes;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, rows * G::kRowBytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < G::kIssues; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + (i * kWaves + wave) * 1024), 16, voff[i],
+                                               0, 0, 0);
 #endif
   }
 };
@@ -244,7 +255,8 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[2], int key0, int lim,
       p[e] = __builtin_amdgcn_exp2f(fmaf(s[b][r0 + e], c_log2, neg_m));
       l4[e] += p[e];
     }
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    // the old bytes 2, 3 kept by this conversion are replaced by the next one
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[w], false);
     pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
   }
   st.l_part = st.l_part * alpha + ((l4[0] + l4[1]) + (l4[2] + l4[3]));
@@ -263,7 +275,8 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
                                      int j, const i32x8 (&qf)[D / 64], f32x16 (&s_in)[2], f32x16 (&s_out)[2],
                                      const i32x8& p_in, i32x8& p_out, RowState8<D>& st) {
   constexpr int kN = D / 32;            // S MFMAs (k-step, block) = P V MFMAs (column tiles)
-  asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  if constexpr (Geom8<D>::kIssues == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
@@ -418,7 +431,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
   f32x16 sa[2], sb[2];
   i32x8 pa = i32x8{0, 0, 0, 0, 0, 0, 0, 0}, pb = pa;
 
-  asm volatile("s_waitcnt vmcnt(2)" ::: "memory");   // K_0, K_1 (Q's loads are older still)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the prologue's copies and Q
   __syncthreads();
   scores<D>(lds + G::k_buf(0), c, qf, sa);
 
@@ -644,6 +657,21 @@ extern "C" int fa_quant_fp8(const void* x, void* x8, float* descale, int B, int 
   const float inv_sqrt_d = (float)(1.0 / sqrt((double)d));
   hipLaunchKernelGGL(fp8_descale_kernel, dim3(small), dim3(256), 0, stream, descale, (int)bh, rotate, inv_sqrt_d);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_fwd_fp8_tile(int B, int H, int N, int d, int causal, int* rows_per_block, int* keys_per_tile,
+                               int* waves, long long* blocks) {
+  long long bh = 0;
+  const int st = check_shape8(B, H, N, d, &bh);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_FLAG;
+  const long long nqb = ((long long)N + kBR - 1) / kBR;
+  if (bh * nqb * kThreads > 0xffffffffLL) return FA_ERR_SHAPE;
+  if (rows_per_block) *rows_per_block = kBR;
+  if (keys_per_tile) *keys_per_tile = kBC;
+  if (waves) *waves = kWaves;
+  if (blocks) *blocks = bh * nqb;
+  return FA_OK;
 }
 
 extern "C" int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_descale,

@@ -25,8 +25,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_fa1order", "fa_fwd_fp8", "fa_fwd_splitkv",
-                                    "fa_fwd_splitkv_plan", "fa_fwd_tile", "fa_quant_fp8", "fa_status_str"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_fa1order", "fa_fwd_fp8", "fa_fwd_fp8_tile",
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_fwd_tile", "fa_quant_fp8",
+                                    "fa_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -193,4 +194,12 @@ def call_fp8(q=Q, k=K, v=V, qd=DQ, kd=DK, vd=DV, o=O, lse=L, B=1, H=1, N=16, d=6
 ])
 def test_bad_fwd_fp8_arguments_are_rejected_on_the_host(lib, kw, code):
     assert call_fp8(**kw) == code
+
+
+def test_fp8_launch_shape_query(lib):
+    rows, keys, waves, blocks = fa.fa_fwd_fp8_tile(1, 32, 16384, 128, 1)
+    assert (rows, keys, waves) == (128, 64, 4) and blocks == 32 * 16384 // 128
+    assert fa.fa_fwd_fp8_tile(2, 3, 1000, 64, 0)[3] == 6 * 8
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_fp8_tile(1, 1, 16, 96, 0)
 

@@ -213,7 +213,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  *             (bit c of sign_lo for c < 64, bit c - 64 of sign_hi otherwise;
  *             bits at or past d are ignored).
  *   stream    HIP stream.
- * Four kernels run in order on `stream` (clear, amax, quantise, descale);
+ * Four kernels run in order on `stream`: workgroup maxima (kept in x8 until
+ * the codes overwrite them), per-head amax, codes, factors.  No atomics;
  * codes and factors are bitwise reproducible.  Returns FA_OK or FA_ERR_NULL,
  * _SHAPE, _HEAD_DIM, _FLAG (rotate not 0/1), _ALIGN, _ALIAS, _LAUNCH.
  */

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 LIB_NAME = "libfa_mi355x.so"
-SOURCES = [os.path.join(PKG, "csrc", name) for name in ("fa_fwd.hip", "fa_bwd.hip", "fa_fa1.hip", "fa_fp8.hip")]
+SOURCES = [os.path.join(PKG, "csrc", name) for name in ("fa_fwd.hip", "fa_bwd.hip", "fa_fa1.hip", "fa_fp8.hip", "fa_quant8.hip")]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

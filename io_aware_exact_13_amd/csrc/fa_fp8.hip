@@ -5,17 +5,11 @@
 // units at twice the bf16 rate, with incoherent processing against the
 // quantisation error.  The page gives no scheme; the one implemented here:
 //   * E4M3 operands with one dequantisation factor per (batch, head) and
-//     tensor: code = RNE_e4m3(y * 448 / amax), descale = amax / 448, where
-//     amax is the head's largest |y|.
-//   * Incoherent processing (optional, for Q and K): y = (sigma o x) H, with a
-//     random sign diagonal sigma and the Sylvester-Hadamard matrix H (entries
-//     +-1), by the fast Walsh-Hadamard butterfly in fp32 (widths 1, 2, 4, ...,
-//     each pair (a, b) -> (a + b, a - b)); the 1/sqrt(d) that makes the
-//     rotation orthonormal is folded into the descale.  A shared rotation of
-//     Q and K leaves Q K^T unchanged and spreads outlier channels.
-//   * The forward is the online softmax of the bf16 path with P rounded to
-//     E4M3 instead of bf16, taken against the running row maximum (P <= 1,
-//     the largest weight so far exactly 1); the running sum adds the fp32 P.
+//     tensor, made by fa_quant_fp8 (fa_quant8.hip), Q and K optionally after
+//     a shared random-sign Hadamard rotation that leaves Q K^T unchanged;
+//   * the online softmax of the bf16 path with P rounded to E4M3 instead of
+//     bf16, taken against the running row maximum (P <= 1, the largest
+//     weight so far exactly 1); the running sum adds the fp32 P.
 //
 // gfx950 design:
 //   * Both products run on v_mfma_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32
@@ -68,7 +62,6 @@ constexpr int kBR = kWaves * 32;  // query rows per workgroup
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kE4M3Max = 448.0f;
 
 __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   // format fields 0, 0: both operands E4M3; zero scale operands select the
@@ -472,131 +465,6 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     if (c.h == 0) LSE[(size_t)bh * N + qrow] = (st.m_ref + log2f(l_tot)) * kLn2;
   }
 }
-
-// ------------------------------------------------------------ quantisation
-//
-// Threads take 8 consecutive elements of a row (16 bytes of bf16), D/8
-// threads per row; a 256-thread workgroup covers kQPass rows per pass and
-// kQIter passes, all of one head (so each workgroup feeds one amax).
-
-constexpr int kQThreads = 256;
-constexpr int kQIter = 4;
-
-// The row chunk as fp32, with the sign flips and the Walsh-Hadamard
-// butterflies applied when ROT: stages of width 1, 2, 4 inside the thread,
-// 8 .. D/2 across the row's threads (lane xor w/8); the lower element of a
-// pair becomes a + b, the upper a - b, as the oracle's order fixes.
-template <int D, bool ROT>
-__device__ __forceinline__ void row_chunk(const __bf16* __restrict__ X, size_t head_off, int row, int N, int c8,
-                                          uint64_t slo, uint64_t shi, float (&v)[8]) {
-  if (row < N) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(X + head_off + (size_t)row * D + 8 * c8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = __builtin_bit_cast(float, raw[e] << 16);
-      v[2 * e + 1] = __builtin_bit_cast(float, raw[e] & 0xffff0000u);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.f;
-  }
-  if constexpr (ROT) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int bit = 8 * c8 + e;
-      const uint64_t word = bit < 64 ? slo : shi;
-      if ((word >> (bit & 63)) & 1) v[e] = -v[e];
-    }
-#pragma unroll
-    for (int w = 1; w < 8; w <<= 1)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if ((i & w) == 0) {
-          const float a = v[i], b = v[i + w];
-          v[i] = a + b;
-          v[i + w] = a - b;
-        }
-#pragma unroll
-    for (int w8 = 1; w8 < D / 8; w8 <<= 1) {
-      const bool upper = (c8 & w8) != 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float other = __shfl_xor(v[e], w8);
-        v[e] = upper ? other - v[e] : v[e] + other;
-      }
-    }
-  }
-}
-
-template <int D, bool ROT>
-__global__ __launch_bounds__(kQThreads) void fp8_amax_kernel(const __bf16* __restrict__ X, float* __restrict__ amax,
-                                                             int N, int nrb, uint64_t slo, uint64_t shi) {
-  constexpr int kPer = D / 8, kPass = kQThreads / kPer;
-  const int bh = blockIdx.x / nrb, rb = blockIdx.x % nrb;
-  const int tid = threadIdx.x, c8 = tid % kPer;
-  const size_t head_off = (size_t)bh * N * D;
-  float m = 0.f;
-#pragma unroll
-  for (int it = 0; it < kQIter; ++it) {
-    float v[8];
-    row_chunk<D, ROT>(X, head_off, rb * kPass * kQIter + it * kPass + tid / kPer, N, c8, slo, shi, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  __shared__ float wm[kQThreads / 64];
-  if ((tid & 63) == 0) wm[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < kQThreads / 64; ++w) m = fmaxf(m, wm[w]);
-    // non-negative floats order like their bit patterns
-    atomicMax(reinterpret_cast<unsigned int*>(amax + bh), __builtin_bit_cast(unsigned int, m));
-  }
-}
-
-template <int D, bool ROT>
-__global__ __launch_bounds__(kQThreads) void fp8_quant_kernel(const __bf16* __restrict__ X, uint8_t* __restrict__ X8,
-                                                              const float* __restrict__ amax, int N, int nrb,
-                                                              uint64_t slo, uint64_t shi) {
-  constexpr int kPer = D / 8, kPass = kQThreads / kPer;
-  const int bh = blockIdx.x / nrb, rb = blockIdx.x % nrb;
-  const int tid = threadIdx.x, c8 = tid % kPer;
-  const size_t head_off = (size_t)bh * N * D;
-  const float am = amax[bh];
-  const float s = am > 0.f ? kE4M3Max / am : 1.f;
-#pragma unroll
-  for (int it = 0; it < kQIter; ++it) {
-    const int row = rb * kPass * kQIter + it * kPass + tid / kPer;
-    float v[8];
-    row_chunk<D, ROT>(X, head_off, row, N, c8, slo, shi, v);
-    if (row < N) {
-      u32x2 w;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h] * s, v[4 * h + 1] * s, 0, false);
-        w[h] = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h + 2] * s, v[4 * h + 3] * s, lo, true);
-      }
-      *reinterpret_cast<u32x2*>(X8 + head_off + (size_t)row * D + 8 * c8) = w;
-    }
-  }
-}
-
-__global__ void fp8_fill_kernel(float* __restrict__ p, int n, float value) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = value;
-}
-
-// amax -> descale in place: amax / 448, times 1/sqrt(d) after a rotation.
-__global__ void fp8_descale_kernel(float* __restrict__ p, int n, int rot, float inv_sqrt_d) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) {
-    float dsc = p[i] / kE4M3Max;
-    if (rot) dsc = dsc * inv_sqrt_d;
-    p[i] = dsc;
-  }
-}
-
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
@@ -613,51 +481,6 @@ int check_shape8(int B, int H, int N, int d, long long* bh_out) {
 }
 
 }  // namespace
-
-extern "C" int fa_quant_fp8(const void* x, void* x8, float* descale, int B, int H, int N, int d, int rotate,
-                            uint64_t sign_lo, uint64_t sign_hi, hipStream_t stream) {
-  if (!x || !x8 || !descale) return FA_ERR_NULL;
-  long long bh = 0;
-  const int st = check_shape8(B, H, N, d, &bh);
-  if (st != FA_OK) return st;
-  if (rotate != 0 && rotate != 1) return FA_ERR_FLAG;
-  if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(x8) & 7u) ||
-      (reinterpret_cast<uintptr_t>(descale) & 3u))
-    return FA_ERR_ALIGN;
-  const size_t elems = (size_t)bh * N * d;
-  if (overlaps(x8, elems, x, 2 * elems) || overlaps(descale, (size_t)bh * 4, x, 2 * elems) ||
-      overlaps(descale, (size_t)bh * 4, x8, elems))
-    return FA_ERR_ALIAS;
-  const int rows_per_wg = (kQThreads * 8 / d) * kQIter;
-  const long long nrb = ((long long)N + rows_per_wg - 1) / rows_per_wg;
-  if (nrb * bh > 0x7fffffffLL / kQThreads) return FA_ERR_SHAPE;
-  const unsigned grid = (unsigned)(nrb * bh);
-  const unsigned small = (unsigned)((bh + 255) / 256);
-  const __bf16* X = static_cast<const __bf16*>(x);
-  uint8_t* X8 = static_cast<uint8_t*>(x8);
-  hipLaunchKernelGGL(fp8_fill_kernel, dim3(small), dim3(256), 0, stream, descale, (int)bh, 0.f);
-  // descale holds amax until the last kernel turns it into the factor
-  if (d == 128) {
-    if (rotate) {
-      hipLaunchKernelGGL((fp8_amax_kernel<128, true>), dim3(grid), dim3(kQThreads), 0, stream, X, descale, N, (int)nrb, sign_lo, sign_hi);
-      hipLaunchKernelGGL((fp8_quant_kernel<128, true>), dim3(grid), dim3(kQThreads), 0, stream, X, X8, descale, N, (int)nrb, sign_lo, sign_hi);
-    } else {
-      hipLaunchKernelGGL((fp8_amax_kernel<128, false>), dim3(grid), dim3(kQThreads), 0, stream, X, descale, N, (int)nrb, sign_lo, sign_hi);
-      hipLaunchKernelGGL((fp8_quant_kernel<128, false>), dim3(grid), dim3(kQThreads), 0, stream, X, X8, descale, N, (int)nrb, sign_lo, sign_hi);
-    }
-  } else {
-    if (rotate) {
-      hipLaunchKernelGGL((fp8_amax_kernel<64, true>), dim3(grid), dim3(kQThreads), 0, stream, X, descale, N, (int)nrb, sign_lo, sign_hi);
-      hipLaunchKernelGGL((fp8_quant_kernel<64, true>), dim3(grid), dim3(kQThreads), 0, stream, X, X8, descale, N, (int)nrb, sign_lo, sign_hi);
-    } else {
-      hipLaunchKernelGGL((fp8_amax_kernel<64, false>), dim3(grid), dim3(kQThreads), 0, stream, X, descale, N, (int)nrb, sign_lo, sign_hi);
-      hipLaunchKernelGGL((fp8_quant_kernel<64, false>), dim3(grid), dim3(kQThreads), 0, stream, X, X8, descale, N, (int)nrb, sign_lo, sign_hi);
-    }
-  }
-  const float inv_sqrt_d = (float)(1.0 / sqrt((double)d));
-  hipLaunchKernelGGL(fp8_descale_kernel, dim3(small), dim3(256), 0, stream, descale, (int)bh, rotate, inv_sqrt_d);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-}
 
 extern "C" int fa_fwd_fp8_tile(int B, int H, int N, int d, int causal, int* rows_per_block, int* keys_per_tile,
                                int* waves, long long* blocks) {

@@ -39,32 +39,35 @@ METRIC = "attention fwd TFLOPS & % of MI355X bf16 MFMA peak at N=16K,d=128 (1 GP
 METRIC_BWD = "attention bwd TFLOPS (5 products, 2.5x fwd FLOPs) & % of MI355X bf16 MFMA peak (1 GPU)"
 METRIC_FP8 = "attention fwd FP8 (E4M3) TFLOPS & % of MI355X fp8 MFMA peak at N=16K,d=128 (1 GPU)"
 
-KERNEL_SOURCE = os.path.join(ROOT, "io_aware_exact_13_amd", "csrc", "fa_fwd.hip")
+KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "fwd_fp8": "fa_fp8.hip"}
 
 # HBM traffic per launch from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same
 # counter reads for a plain 512 MiB device copy (FETCH_SIZE reads half of the
-# bytes the copy moves, WRITE_SIZE all of them).  Keyed by workload; each entry
-# records the sha256 of the kernel source the counters were taken on, and is
-# reported only while that source is unchanged.
+# bytes the copy moves, WRITE_SIZE all of them).  Keyed by workload and pass;
+# each entry records the sha256 of the kernel source the counters were taken
+# on, and is reported only while that source is unchanged.
 FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
-    # workload: (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "causal_b1h32_n16384_d128": (
+    # (workload, pass): (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    ("causal_b1h32_n16384_d128", "fwd"): (
         "463bd7e11e13c6d0f99443af08ca97264f47c34b21a0366b9131b282b22dff65", 3.43241e5, 1.33120e5),
+    ("causal_b1h32_n16384_d128", "fwd_fp8"): (
+        "6addc8431851f10bd8ad68caa9acb616977a5db7cffef281a017bb789fc716d3", 1.54656e5, 1.33153e5),
 }
 
 
-def kernel_source_sha256():
+def kernel_source_sha256(pass_="fwd"):
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
+    path = os.path.join(ROOT, "io_aware_exact_13_amd", "csrc", KERNEL_SOURCES[pass_])
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(name):
-    entry = MEASURED_TRAFFIC.get(name)
-    if entry is None or entry[0] != kernel_source_sha256():
+def measured_traffic(name, pass_="fwd"):
+    entry = MEASURED_TRAFFIC.get((name, pass_))
+    if entry is None or entry[0] != kernel_source_sha256(pass_):
         return None
     return round(entry[1] * 1024 * FETCH_SCALE + entry[2] * 1024 * WRITE_SCALE)
 
@@ -337,7 +340,8 @@ def main():
                 log(f"[bench-all] {sw.name:32s} {'fwd' if ns == 0 else f'split{ns}':>7s} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s{'  (plan)' if ns == plan else ''}")
 
-    traffic = None if (args.bwd or args.splitkv or args.fa1order or args.fp8) else measured_traffic(name)
+    traffic = (None if (args.bwd or args.splitkv or args.fa1order) else
+               measured_traffic(name, "fwd_fp8" if args.fp8 else "fwd"))
     result = {
         "metric": METRIC_BWD if args.bwd else (METRIC_FP8 if args.fp8 else METRIC),
         "value": round(value, 2),

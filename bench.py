@@ -52,7 +52,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # (workload, pass): (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     ("causal_b1h32_n16384_d128", "fwd"): (
-        "463bd7e11e13c6d0f99443af08ca97264f47c34b21a0366b9131b282b22dff65", 3.43241e5, 1.33120e5),
+        "1679157c3a87453ad6e6816609f2c22edb21603b196c421f1a70ee27fa66d9bf", 3.48832e5, 1.33120e5),
     ("causal_b1h32_n16384_d128", "fwd_fp8"): (
         "6addc8431851f10bd8ad68caa9acb616977a5db7cffef281a017bb789fc716d3", 1.54656e5, 1.33153e5),
 }

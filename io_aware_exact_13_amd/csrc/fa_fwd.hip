@@ -29,8 +29,10 @@
 //     permutation by ds_read_b64_tr_b16, which reads V in its natural
 //     row-major LDS layout and hands each lane 4 consecutive keys of one
 //     column.
-//   * Workgroup: 8 waves (two per SIMD) of 32 query rows each, 256 rows;
-//     K/V tiles of 64 keys.  K and V go HBM -> LDS with buffer_load ... lds
+//   * Workgroup: 8 waves (two per SIMD) of 32 query rows each, 256 rows, at
+//     d = 128; at d = 64, where the rings take 64 KiB of LDS, 4 waves and
+//     128 rows, two workgroups per CU (their waves drift apart on the shared
+//     SIMDs: 4% faster there).  K/V tiles of 64 keys.  K and V go HBM -> LDS with buffer_load ... lds
 //     (no VGPR staging; the buffer's record count zero-fills rows past the
 //     last key the workgroup can see), each through a ring of four LDS
 //     buffers, copied two steps before use.  One workgroup barrier per tile.
@@ -74,9 +76,14 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int kBC = 64;           // keys per K/V tile
-constexpr int kWaves = 8;         // waves per workgroup, 32 query rows each
-constexpr int kThreads = kWaves * 64;
-constexpr int kBR = kWaves * 32;  // query rows per workgroup
+// Waves per workgroup (32 query rows each): 8 at d = 128 (one workgroup per
+// CU, 128 KiB of LDS), 4 at d = 64 (64 KiB, two workgroups per CU, whose
+// waves share the SIMDs and drift apart).
+template <int D> constexpr int kWavesOf = D == 64 ? 4 : 8;
+template <int D> constexpr int kThreadsOf = kWavesOf<D> * 64;
+template <int D> constexpr int kBROf = kWavesOf<D> * 32;   // query rows per workgroup
+__host__ __device__ constexpr int rows_per_block(int d) { return d == 64 ? kBROf<64> : kBROf<128>; }
+__host__ __device__ constexpr int threads_per_block(int d) { return d == 64 ? kThreadsOf<64> : kThreadsOf<128>; }
 constexpr int kXcds = 8;
 constexpr int kMaxSplits = 64;    // key ranges per query block in the split-KV forward          // accelerator dies; workgroups are dealt to them round-robin
 constexpr float kLog2e = 1.4426950408889634f;
@@ -104,17 +111,17 @@ struct Geom {
   // V buffer b relative to the V region, whose start is folded into the
   // lanes' V read offsets so that every LDS read immediate stays below 64 KiB
   __host__ __device__ static constexpr int v_rel(int b) { return b * kTile; }
-  static constexpr int kLoads = kTile / (kThreads * 16);    // 1 KiB copies per wave per tile
-  static_assert(kLoads * kThreads * 16 == kTile, "tile not a whole number of wave copies");
+  static constexpr int kLoads = kTile / (kThreadsOf<D> * 16);    // 1 KiB copies per wave per tile
+  static_assert(kLoads * kThreadsOf<D> * 16 == kTile, "tile not a whole number of wave copies");
   __host__ __device__ static constexpr int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
   __host__ __device__ static constexpr int fv(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 };
 
 // One thread's share of the HBM -> LDS copy of a tile (buffer_load ... lds).
-// Copy i of wave w fills the 1 KiB of LDS at base + (kWaves i + w) KiB, lane t
+// Copy i of wave w fills the 1 KiB of LDS at base + (W i + w) KiB (W waves), lane t
 // the 16 bytes at + 16 t, so each lane fetches the global chunk that the
 // swizzle puts in its slot.  The swizzle of a slot's row does not depend on
-// i, so copy i reads at the lane's offset plus i * kWaves KiB.
+// i, so copy i reads at the lane's offset plus i * W KiB.
 template <int D, bool IS_V>
 struct TileCopy {
   unsigned voff;
@@ -139,8 +146,8 @@ struct TileCopy {
     const char* base = head + (size_t)min(key0, n) * G::kRowBytes;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, rows * G::kRowBytes, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + (i * kWaves + wave) * 1024), 16,
-                                             voff + i * kWaves * 1024, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + (i * kWavesOf<D> + wave) * 1024), 16,
+                                             voff + i * kWavesOf<D> * 1024, 0, 0, 0);
 #endif
   }
 };
@@ -506,7 +513,7 @@ __device__ __forceinline__ void step_quad(const Ctx<D>& c, int j, const bf16x8 (
 // fa_merge_kernel combines them.  Otherwise it covers all the tiles and
 // writes O (bf16) and LSE.
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                    float* __restrict__ Opart, float* __restrict__ Lpart,
@@ -536,6 +543,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int qi = SPLIT ? (logical % per_head) / n_splits : logical % per_head;
   const int split = SPLIT ? (logical % per_head) % n_splits : 0;
   const int qb = CAUSAL ? (n_qblocks - 1 - qi) : qi;
+  constexpr int kBR = kBROf<D>;
   const int q0 = qb * kBR;
   const int qrow = q0 + c.wave * 32 + l32;   // this lane's query
   c.N = N;
@@ -597,7 +605,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     c.kcopy.issue(c.Kh, (j0 + 2) * kBC, c.kv_end, lds + G::k_buf(2), c.wave, i);
     c.vcopy.issue(c.Vh, j0 * kBC, c.kv_end, lds + G::v_buf(0), c.wave, i);
   }
-  for (int i = tid; i < G::kTile / 8; i += kThreads)   // V_{-1} = 0
+  for (int i = tid; i < G::kTile / 8; i += kThreadsOf<D>)   // V_{-1} = 0
     reinterpret_cast<u32x2*>(lds + G::v_buf(G::kRing - 1))[i] = u32x2{0u, 0u};
 
   // Q^T operand: lane holds Q[qrow][16*ks + 8*h .. +7] for each k-step
@@ -760,10 +768,11 @@ static int check_shape(int B, int H, int N, int d, int causal, long long* blocks
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
   const long long bh = (long long)B * H;
+  const int kBR = rows_per_block(d);
   const long long nqb = ((long long)N + kBR - 1) / kBR;
   const long long g = bh * nqb;
   // grid size in work-items must fit 32 bits; heads must index in int
-  if (bh > 0x7fffffffLL || g * kThreads > 0xffffffffLL) return FA_ERR_SHAPE;
+  if (bh > 0x7fffffffLL || g * threads_per_block(d) > 0xffffffffLL) return FA_ERR_SHAPE;
   // one head's K or V must stay below 2 GiB (buffer offsets are 32-bit)
   if ((long long)N * d * 2 >= 0x80000000LL) return FA_ERR_SHAPE;
   *blocks = g;
@@ -775,9 +784,9 @@ extern "C" int fa_fwd_tile(int B, int H, int N, int d, int causal, int* rows_per
   long long g = 0;
   const int st = check_shape(B, H, N, d, causal, &g);
   if (st != FA_OK) return st;
-  if (rows_per_block) *rows_per_block = kBR;
+  if (rows_per_block) *rows_per_block = ::rows_per_block(d);
   if (keys_per_tile) *keys_per_tile = kBC;
-  if (waves) *waves = kWaves;
+  if (waves) *waves = threads_per_block(d) / 64;
   if (blocks) *blocks = g;
   return FA_OK;
 }
@@ -800,13 +809,13 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
     return FA_ERR_ALIAS;
 
   const int BH = B * H;
-  const int nqb = (N + kBR - 1) / kBR;
+  const int nqb = (N + rows_per_block(d) - 1) / rows_per_block(d);
   const float c_log2 = scale * kLog2e;
   const __bf16* Q = static_cast<const __bf16*>(q);
   const __bf16* Kp = static_cast<const __bf16*>(k);
   const __bf16* Vp = static_cast<const __bf16*>(v);
   __bf16* Op = static_cast<__bf16*>(o);
-  const dim3 grid((unsigned)blocks), block(kThreads);
+  const dim3 grid((unsigned)blocks), block(threads_per_block(d));
   float* np = nullptr;
   if (d == 128) {
     if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
@@ -845,7 +854,7 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   const int st = check_shape(B, H, N, d, causal, &blocks);
   if (st != FA_OK) return st;
   if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_SPLITS;
-  if (blocks * n_splits * kThreads > 0xffffffffLL) return FA_ERR_SHAPE;
+  if (blocks * n_splits * threads_per_block(d) > 0xffffffffLL) return FA_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
@@ -866,7 +875,7 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   }
 
   const int BH = B * H;
-  const int nqb = (N + kBR - 1) / kBR;
+  const int nqb = (N + rows_per_block(d) - 1) / rows_per_block(d);
   const float c_log2 = scale * kLog2e;
   const __bf16* Q = static_cast<const __bf16*>(q);
   const __bf16* Kp = static_cast<const __bf16*>(k);
@@ -874,7 +883,7 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   __bf16* Op = static_cast<__bf16*>(o);
   __bf16* nb = nullptr;
   float* nl = nullptr;
-  const dim3 grid((unsigned)(blocks * n_splits)), block(kThreads);
+  const dim3 grid((unsigned)(blocks * n_splits)), block(threads_per_block(d));
   if (d == 128) {
     if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
     else        hipLaunchKernelGGL((fa_fwd_kernel<128, false, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);

@@ -39,6 +39,11 @@
 
 namespace {
 
+// Waves per SIMD the two gradient kernels are compiled for: 2 at d = 128
+// (about 240 registers a lane), 3 at d = 64, whose kernels fit in 168
+// registers (5% faster on the 2K d = 64 workload than at 2).
+template <int D> constexpr int kWavesPerSimd = D == 64 ? 3 : 2;
+
 using namespace cdna4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const __bf16* __restr
 //   P    = exp2(S^T c - LSE log2 e),  dS = P (dP - D)   (masked keys give 0)
 //   dQ^T += K^T dS^T                      (A: K^T by transposed reads; B: dS from registers)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWavesPerSimd<D>))) void fa_bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dQ, int BH, int N, int n_qblocks, float c_log2, float scale) {
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 //   P  = exp2(S c - LSE log2 e),  dS = P (dP - D)      (rows past N or above the key give 0)
 //   dV^T += dO^T P,  dK^T += Q^T dS       (A: dO^T, Q^T by transposed reads; B: P, dS)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWavesPerSimd<D>))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int N, int n_kblocks, float c_log2,

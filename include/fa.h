@@ -201,7 +201,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  *
  *   x         bf16 input, [B][H][N][d] contiguous, 16-byte aligned.  Read
  *             only.  Values must be finite.
- *   x8        E4M3 codes, same layout (one byte per element), 8-byte
+ *   x8        E4M3 codes, same layout (one byte per element), 16-byte
  *             aligned; fully overwritten.
  *   descale   fp32 [B][H], 4-byte aligned; overwritten with each head's
  *             dequantisation factor (0 for an all-zero head, whose codes are

@@ -9,8 +9,8 @@
 //   * code = RNE_e4m3(y * 448 / amax) with amax the head's largest |y|, and
 //     descale = amax / 448 (times 1/sqrt(d) after a rotation);
 //   * rotation y = (sigma o x) H by the fast Walsh-Hadamard butterfly in
-//     fp32: widths 1, 2, 4 inside a thread, 8 .. d/2 across the row's threads,
-//     each pair (a, b) -> (a + b, a - b).
+//     fp32: widths 1 .. 16 inside a thread, 32 and 64 across the row's lanes
+//     (DPP quad permutes), each pair (a, b) -> (a + b, a - b).
 // Two passes over the input: the first finds each workgroup's amax and
 // leaves it in the (not yet written) code buffer, a small kernel reduces
 // those per head into `descale`, and the second pass writes the codes; a
@@ -32,54 +32,71 @@ constexpr float kE4M3Max = 448.0f;
 
 // ------------------------------------------------------------ quantisation
 //
-// Threads take 8 consecutive elements of a row (16 bytes of bf16), D/8
-// threads per row; a 256-thread workgroup covers kQPass rows per pass and
-// kQIter passes, all of one head (so each workgroup feeds one amax).
+// Threads take 32 consecutive elements of a row (64 bytes of bf16), D/32
+// threads per row (a quad of lanes at d = 128, a pair at d = 64); a 256-thread
+// workgroup covers kQPass rows per pass and kQIter passes, all of one head
+// (so each workgroup feeds one amax).
 
 constexpr int kQThreads = 256;
-constexpr int kQIter = 4;
+constexpr int kQIter = 2;
+constexpr int kQElems = 32;
+
+// Sign words of the lane's 32 columns: bit 31 set where the rotation
+// negates the column (bit c of the 128-bit mask).
+__device__ __forceinline__ void sign_words(int col0, uint64_t slo, uint64_t shi, unsigned (&sg)[kQElems]) {
+#pragma unroll
+  for (int e = 0; e < kQElems; ++e) {
+    const int bit = col0 + e;
+    const uint64_t word = bit < 64 ? slo : shi;
+    sg[e] = (unsigned)((word >> (bit & 63)) & 1) << 31;
+  }
+}
 
 // The row chunk as fp32, with the sign flips and the Walsh-Hadamard
-// butterflies applied when ROT: stages of width 1, 2, 4 inside the thread,
-// 8 .. D/2 across the row's threads (lane xor w/8); the lower element of a
-// pair becomes a + b, the upper a - b, as the oracle's order fixes.
+// butterflies applied when ROT: stages of width 1 .. 16 inside the thread,
+// 32 and 64 across the row's lanes (lane xor 1, xor 2, by DPP quad
+// permutes).  The lower element of a pair becomes a + b, the upper a - b, as
+// the oracle's order fixes; across lanes that is fma(+-1, v, other), whose
+// product is exact, so the sum is rounded once as a + b or a - b would be.
 template <int D, bool ROT>
-__device__ __forceinline__ void row_chunk(const __bf16* __restrict__ X, size_t head_off, int row, int N, int c8,
-                                          uint64_t slo, uint64_t shi, float (&v)[8]) {
+__device__ __forceinline__ void row_chunk(const __bf16* __restrict__ X, size_t head_off, int row, int N, int c,
+                                          const unsigned (&sg)[kQElems], float (&v)[kQElems]) {
   if (row < N) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(X + head_off + (size_t)row * D + 8 * c8);
+    const u32x4* src = reinterpret_cast<const u32x4*>(X + head_off + (size_t)row * D + kQElems * c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = __builtin_bit_cast(float, raw[e] << 16);
-      v[2 * e + 1] = __builtin_bit_cast(float, raw[e] & 0xffff0000u);
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 raw = src[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * q + 2 * e] = __builtin_bit_cast(float, raw[e] << 16);
+        v[8 * q + 2 * e + 1] = __builtin_bit_cast(float, raw[e] & 0xffff0000u);
+      }
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    for (int e = 0; e < kQElems; ++e) v[e] = 0.f;
   }
   if constexpr (ROT) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int bit = 8 * c8 + e;
-      const uint64_t word = bit < 64 ? slo : shi;
-      if ((word >> (bit & 63)) & 1) v[e] = -v[e];
-    }
+    for (int e = 0; e < kQElems; ++e) v[e] = __builtin_bit_cast(float, __builtin_bit_cast(unsigned, v[e]) ^ sg[e]);
 #pragma unroll
-    for (int w = 1; w < 8; w <<= 1)
+    for (int w = 1; w < kQElems; w <<= 1)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kQElems; ++i)
         if ((i & w) == 0) {
           const float a = v[i], b = v[i + w];
           v[i] = a + b;
           v[i + w] = a - b;
         }
 #pragma unroll
-    for (int w8 = 1; w8 < D / 8; w8 <<= 1) {
-      const bool upper = (c8 & w8) != 0;
+    for (int m = 1; m < D / kQElems; m <<= 1) {
+      const float sgn = (c & m) ? -1.f : 1.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float other = __shfl_xor(v[e], w8);
-        v[e] = upper ? other - v[e] : v[e] + other;
+      for (int e = 0; e < kQElems; ++e) {
+        const int bits = __builtin_bit_cast(int, v[e]);
+        const int ob = m == 1 ? __builtin_amdgcn_mov_dpp(bits, 0xB1, 0xF, 0xF, true)    // quad_perm [1,0,3,2]
+                              : __builtin_amdgcn_mov_dpp(bits, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+        v[e] = fmaf(sgn, v[e], __builtin_bit_cast(float, ob));
       }
     }
   }
@@ -90,17 +107,19 @@ __device__ __forceinline__ void row_chunk(const __bf16* __restrict__ X, size_t h
 template <int D, bool ROT>
 __global__ __launch_bounds__(kQThreads) void fp8_amax_kernel(const __bf16* __restrict__ X, uint8_t* __restrict__ X8,
                                                              int N, int nrb, uint64_t slo, uint64_t shi) {
-  constexpr int kPer = D / 8, kPass = kQThreads / kPer;
+  constexpr int kPer = D / kQElems, kPass = kQThreads / kPer;
   const int bh = blockIdx.x / nrb, rb = blockIdx.x % nrb;
-  const int tid = threadIdx.x, c8 = tid % kPer;
+  const int tid = threadIdx.x, c = tid % kPer;
   const size_t head_off = (size_t)bh * N * D;
+  unsigned sg[kQElems];
+  sign_words(kQElems * c, slo, shi, sg);
   float m = 0.f;
 #pragma unroll
   for (int it = 0; it < kQIter; ++it) {
-    float v[8];
-    row_chunk<D, ROT>(X, head_off, rb * kPass * kQIter + it * kPass + tid / kPer, N, c8, slo, shi, v);
+    float v[kQElems];
+    row_chunk<D, ROT>(X, head_off, rb * kPass * kQIter + it * kPass + tid / kPer, N, c, sg, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    for (int e = 0; e < kQElems; ++e) m = fmaxf(m, fabsf(v[e]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -132,25 +151,29 @@ template <int D, bool ROT>
 __global__ __launch_bounds__(kQThreads) void fp8_quant_kernel(const __bf16* __restrict__ X, uint8_t* __restrict__ X8,
                                                               const float* __restrict__ amax, int N, int nrb,
                                                               uint64_t slo, uint64_t shi) {
-  constexpr int kPer = D / 8, kPass = kQThreads / kPer;
+  constexpr int kPer = D / kQElems, kPass = kQThreads / kPer;
   const int bh = blockIdx.x / nrb, rb = blockIdx.x % nrb;
-  const int tid = threadIdx.x, c8 = tid % kPer;
+  const int tid = threadIdx.x, c = tid % kPer;
   const size_t head_off = (size_t)bh * N * D;
   const float am = amax[bh];
   const float s = am > 0.f ? kE4M3Max / am : 1.f;
+  unsigned sg[kQElems];
+  sign_words(kQElems * c, slo, shi, sg);
 #pragma unroll
   for (int it = 0; it < kQIter; ++it) {
     const int row = rb * kPass * kQIter + it * kPass + tid / kPer;
-    float v[8];
-    row_chunk<D, ROT>(X, head_off, row, N, c8, slo, shi, v);
+    float v[kQElems];
+    row_chunk<D, ROT>(X, head_off, row, N, c, sg, v);
     if (row < N) {
-      u32x2 w;
+      u32x4 w[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h] * s, v[4 * h + 1] * s, 0, false);
-        w[h] = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * h + 2] * s, v[4 * h + 3] * s, lo, true);
+      for (int q = 0; q < 8; ++q) {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q] * s, v[4 * q + 1] * s, 0, false);
+        w[q >> 2][q & 3] = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q + 2] * s, v[4 * q + 3] * s, lo, true);
       }
-      *reinterpret_cast<u32x2*>(X8 + head_off + (size_t)row * D + 8 * c8) = w;
+      u32x4* dst = reinterpret_cast<u32x4*>(X8 + head_off + (size_t)row * D + kQElems * c);
+      dst[0] = w[0];
+      dst[1] = w[1];
     }
   }
 }
@@ -188,14 +211,14 @@ extern "C" int fa_quant_fp8(const void* x, void* x8, float* descale, int B, int 
   const int st = check_shape8(B, H, N, d, &bh);
   if (st != FA_OK) return st;
   if (rotate != 0 && rotate != 1) return FA_ERR_FLAG;
-  if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(x8) & 7u) ||
+  if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(x8) & 15u) ||
       (reinterpret_cast<uintptr_t>(descale) & 3u))
     return FA_ERR_ALIGN;
   const size_t elems = (size_t)bh * N * d;
   if (overlaps(x8, elems, x, 2 * elems) || overlaps(descale, (size_t)bh * 4, x, 2 * elems) ||
       overlaps(descale, (size_t)bh * 4, x8, elems))
     return FA_ERR_ALIAS;
-  const int rows_per_wg = (kQThreads * 8 / d) * kQIter;
+  const int rows_per_wg = (kQThreads * kQElems / d) * kQIter;
   const long long nrb = ((long long)N + rows_per_wg - 1) / rows_per_wg;
   if (nrb * bh > 0x7fffffffLL / kQThreads) return FA_ERR_SHAPE;
   const unsigned grid = (unsigned)(nrb * bh);

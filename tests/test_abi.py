@@ -173,7 +173,8 @@ def call_quant(x=Q, x8=X8, descale=DS, B=1, H=1, N=16, d=64, rotate=0):
     (dict(x=0), fa.FA_ERR_NULL), (dict(x8=0), fa.FA_ERR_NULL), (dict(descale=0), fa.FA_ERR_NULL),
     (dict(B=0), fa.FA_ERR_SHAPE), (dict(N=-3), fa.FA_ERR_SHAPE), (dict(B=1 << 20, H=1 << 20), fa.FA_ERR_SHAPE),
     (dict(d=96), fa.FA_ERR_HEAD_DIM), (dict(rotate=2), fa.FA_ERR_FLAG),
-    (dict(x=Q + 8), fa.FA_ERR_ALIGN), (dict(x8=X8 + 4), fa.FA_ERR_ALIGN), (dict(descale=DS + 2), fa.FA_ERR_ALIGN),
+    (dict(x=Q + 8), fa.FA_ERR_ALIGN), (dict(x8=X8 + 4), fa.FA_ERR_ALIGN), (dict(x8=X8 + 8), fa.FA_ERR_ALIGN),
+    (dict(descale=DS + 2), fa.FA_ERR_ALIGN),
     (dict(x8=Q + 512), fa.FA_ERR_ALIAS), (dict(descale=X8 + 8), fa.FA_ERR_ALIAS), (dict(descale=Q), fa.FA_ERR_ALIAS),
 ])
 def test_bad_quant_fp8_arguments_are_rejected_on_the_host(lib, kw, code):

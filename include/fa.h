@@ -185,7 +185,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  *   format     OCP FP8 E4M3 (bias 7, largest finite 448, NaN = S.1111.111),
  *              round to nearest even;
  *   scaling    one factor per (batch, head) and tensor: amax = max |y| over
- *              the head, code = E4M3(y * 448 / amax), descale = amax / 448;
+ *              the head (at least 2^-117 unless 0), code = E4M3(y * 448 /
+ *              amax), descale = amax / 448;
  *   rotation   optional for Q and K: y = (sigma o x) H with sigma a random
  *              sign diagonal and H the Sylvester-Hadamard matrix (+-1
  *              entries), computed by the fast Walsh-Hadamard butterfly in

@@ -6,8 +6,9 @@
 // Attention 3 (FP8 low-precision support): FP8 operands, and incoherent
 // processing against the quantisation error.  The page gives no scheme; the
 // one implemented here:
-//   * code = RNE_e4m3(y * 448 / amax) with amax the head's largest |y|, and
-//     descale = amax / 448 (times 1/sqrt(d) after a rotation);
+//   * code = RNE_e4m3(y * 448 / amax) with amax the head's largest |y|
+//     (raised to 2^-117 if smaller and non-zero, so that 448 / amax stays
+//     finite), and descale = amax / 448 (times 1/sqrt(d) after a rotation);
 //   * rotation y = (sigma o x) H by the fast Walsh-Hadamard butterfly in
 //     fp32: widths 1 .. 16 inside a thread, 32 and 64 across the row's lanes
 //     (DPP quad permutes), each pair (a, b) -> (a + b, a - b).
@@ -29,6 +30,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kE4M3Max = 448.0f;
+constexpr float kAmaxMin = 0x1p-117f;   // smallest amax of a non-zero head: 448 / amax stays finite
+
+// The amax a head's scale is taken from: 0 for an all-zero head, else at least 2^-117.
+__device__ __forceinline__ float amax_used(float am) { return am > 0.f ? fmaxf(am, kAmaxMin) : 0.f; }
 
 // ------------------------------------------------------------ quantisation
 //
@@ -155,7 +160,7 @@ __global__ __launch_bounds__(kQThreads) void fp8_quant_kernel(const __bf16* __re
   const int bh = blockIdx.x / nrb, rb = blockIdx.x % nrb;
   const int tid = threadIdx.x, c = tid % kPer;
   const size_t head_off = (size_t)bh * N * D;
-  const float am = amax[bh];
+  const float am = amax_used(amax[bh]);
   const float s = am > 0.f ? kE4M3Max / am : 1.f;
   unsigned sg[kQElems];
   sign_words(kQElems * c, slo, shi, sg);
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(kQThreads) void fp8_quant_kernel(const __bf16* __re
 __global__ void fp8_descale_kernel(float* __restrict__ p, int n, int rot, float inv_sqrt_d) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
-    float dsc = p[i] / kE4M3Max;
+    float dsc = amax_used(p[i]) / kE4M3Max;
     if (rot) dsc = dsc * inv_sqrt_d;
     p[i] = dsc;
   }

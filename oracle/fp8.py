@@ -18,7 +18,9 @@ rest of the pages support:
     |y| over the head's N x d values, the quantisation multiplier is
     s = 448 / amax (fp32; s = 1 when amax = 0), each code is the E4M3
     rounding of the fp32 product y * s, and the dequantisation factor
-    ("descale") is amax / 448 (fp32).
+    ("descale") is amax / 448 (fp32).  A non-zero amax below 2^-117 is
+    raised to 2^-117 first, so that s stays finite (at most 1.75 2^125) for
+    heads of tiny values such as bf16 subnormals.
   * Incoherent processing (Q and K only, the two operands of the score
     product): every row is multiplied by a random sign diagonal and by the
     d x d Sylvester-Hadamard matrix H (entries +-1) before the amax is
@@ -49,6 +51,7 @@ from __future__ import annotations
 import numpy as np
 
 E4M3_MAX = 448.0
+AMAX_MIN = 2.0 ** -117       # smallest amax used for a non-zero head
 E4M3_MIN_NORMAL = 2.0 ** -6
 E4M3_MIN_SUBNORMAL = 2.0 ** -9
 FP8_TILE = 64
@@ -148,8 +151,8 @@ def quantize_heads(x, rotate: bool = False, sign_bits: int = 0):
     """Per-(batch, head) E4M3 quantisation of x [B, H, N, d] (values exactly
     representable in fp32, e.g. bf16).
 
-    Returns (codes uint8 [B, H, N, d], amax float32 [B, H], descale float32
-    [B, H]).  With `rotate`, each row is first transformed as
+    Returns (codes uint8 [B, H, N, d], amax float32 [B, H] (after the
+    2^-117 floor), descale float32 [B, H]).  With `rotate`, each row is first transformed as
     y = fwht(sigma o x) in fp32 (sigma from sign_bits); see the module
     docstring for the scheme.
     """
@@ -157,6 +160,7 @@ def quantize_heads(x, rotate: bool = False, sign_bits: int = 0):
     B, H, N, d = x32.shape
     y = fwht(x32 * sign_vector(sign_bits, d), np.float32) if rotate else x32
     amax = np.abs(y).reshape(B, H, N * d).max(axis=-1).astype(np.float32)
+    amax = np.where(amax > 0, np.maximum(amax, np.float32(AMAX_MIN)), amax).astype(np.float32)
     s = np.where(amax > 0, np.float32(E4M3_MAX) / np.where(amax > 0, amax, np.float32(1)),
                  np.float32(1)).astype(np.float32)
     prod = (y * s[:, :, None, None]).astype(np.float32)       # one fp32 product per element

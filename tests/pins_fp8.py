@@ -202,6 +202,27 @@ def check_quantize_scaling(f):
         assert np.all(np.abs(deq - yy) <= tol * (1 + 1e-6) + 1e-12)
 
 
+def check_quantize_tiny_heads(f):
+    """A head of bf16 subnormals: 448 / amax would overflow fp32, so amax is
+    raised to 2^-117; every code is finite, the largest |y| maps to
+    448 * amax / 2^-117 (a power-of-two step below 448), and the dequantised
+    values lie within one code step of y.  A head at 2^-117 or above is not
+    affected by the floor (scaling by 2^k keeps its codes)."""
+    x = np.zeros((1, 2, 8, 64), dtype=np.float32)
+    x[0, 0] = np.float32(2.0 ** -130) * np.arange(1, 513, dtype=np.float32).reshape(8, 64) / 512
+    x[0, 1] = np.float32(2.0 ** -100) * np.arange(1, 513, dtype=np.float32).reshape(8, 64) / 512
+    codes, amax, desc = f.quantize_heads(x)
+    assert amax[0, 0] == np.float32(2.0 ** -117) and amax[0, 1] == np.float32(2.0 ** -100)
+    assert np.all(np.isfinite(f.e4m3_decode(codes)))
+    deq = f.dequantize_heads(codes, desc)
+    step = 2.0 ** -3 * np.abs(x.astype(np.float64)) + desc.astype(np.float64)[:, :, None, None] * 2.0 ** -9
+    assert np.all(np.abs(deq - x) <= step)
+    top = f.e4m3_decode(codes[0, 0].ravel()[-1:])[0]
+    assert top == 448.0 * 2.0 ** -13          # 2^-130 * 448 / 2^-117, exact in E4M3
+    c2, _, _ = f.quantize_heads(x * np.float32(2.0 ** 20))
+    assert np.array_equal(c2[0, 1], codes[0, 1])
+
+
 def check_rotation_reduces_outlier_error(f):
     """The purpose stated on the page: with outlier channels shared by Q and K
     (two of 128 channels 20 times larger in both), quantising after the
@@ -299,6 +320,7 @@ def check_fp8_attention_bounds(f):
 
 ALL_CHECKS = [check_e4m3_closed_forms, check_e4m3_round_trip, check_e4m3_nearest_even_brute_force,
               check_e4m3_range_limits, check_hadamard_algebra, check_fwht_fp32_butterfly_order,
-              check_rotation_preserves_scores, check_quantize_scaling, check_rotation_reduces_outlier_error,
+              check_rotation_preserves_scores, check_quantize_scaling, check_quantize_tiny_heads,
+              check_rotation_reduces_outlier_error,
               check_fp8_attention_without_rounding_is_plain, check_fp8_attention_hand_example,
               check_fp8_attention_bounds]

@@ -91,6 +91,22 @@ def test_quantisation_is_bit_exact(B, H, N, d, rotate):
             assert not (g8[0, 0] & 0x7F).any() and gd[0, 0] == 0
 
 
+def test_quantisation_of_tiny_heads_is_bit_exact():
+    """Heads of bf16 subnormals and of values near 2^-117: the amax floor keeps
+    448 / amax finite; codes and factors match the oracle bit for bit."""
+    w = workloads.custom(1, 3, 300, 128, False, seed=6150)
+    q = workloads.make_inputs(w)[0].float()
+    q[0, 0] *= 2.0 ** -133          # bf16 subnormals (and some flushed to zero)
+    q[0, 1] *= 2.0 ** -118
+    x = q.to(torch.bfloat16)
+    signs = workloads.make_fp8_signs(w.seed, w.d)
+    for rotate in (False, True):
+        g8, gd = gpu_quant(x, rotate, signs)
+        c, _, ds = ofp8.quantize_heads(x.float().numpy(), rotate, signs)
+        assert np.array_equal(g8, c) and np.array_equal(gd.view(np.uint32), ds.view(np.uint32))
+        assert np.isfinite(ofp8.e4m3_decode(g8)).all()
+
+
 def test_quantisation_of_peaky_and_outlier_inputs_is_bit_exact():
     for w, maker in ((workloads.custom(1, 2, 2048, 128, True, seed=6101, peaky=True), workloads.make_inputs),
                      (workloads.custom(1, 2, 1024, 128, True, seed=6102), workloads.make_outlier_inputs),

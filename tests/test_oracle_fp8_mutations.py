@@ -26,6 +26,7 @@ MUTATIONS = {
     "amax_without_abs": ("amax = np.abs(y).reshape(B, H, N * d)", "amax = y.reshape(B, H, N * d)"),
     "multiplier_inverted": ("np.float32(E4M3_MAX) / np.where(amax > 0, amax, np.float32(1))",
                             "np.where(amax > 0, amax, np.float32(1)) / np.float32(E4M3_MAX)"),
+    "no_amax_floor": ("np.maximum(amax, np.float32(AMAX_MIN))", "amax"),
     "descale_without_sqrt": ("descale * np.float32(1.0 / np.sqrt(d))", "descale * np.float32(1.0)"),
     "p_not_rounded": ("pr = e4m3_round(p) if round_p else p", "pr = p"),
     "sum_of_rounded_p": ("l = alpha * l + p.sum(axis=1)", "l = alpha * l + pr.sum(axis=1)"),

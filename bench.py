@@ -52,7 +52,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # (workload, pass): (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     ("causal_b1h32_n16384_d128", "fwd"): (
-        "1679157c3a87453ad6e6816609f2c22edb21603b196c421f1a70ee27fa66d9bf", 3.48832e5, 1.33120e5),
+        "05913340d5eb92cac8115d51a9ecdd1daf54cc3750d2f8425458901c7d116856", 3.48992e5, 1.33120e5),
     ("causal_b1h32_n16384_d128", "fwd_fp8"): (
         "abe8d17c666a0d56fb8c12b9825471c41b185aa064b8e840237156406444970d", 1.54652e5, 1.33154e5),
 }

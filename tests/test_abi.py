@@ -138,7 +138,8 @@ def test_splitkv_plan(lib):
     n, ob, lb = fa.fa_fwd_splitkv_plan(1, 4, 16384, 128, 1)
     assert n == 2 and ob == 2 * 4 * 16384 * 128 * 4 and lb == 2 * 4 * 16384 * 4
     assert fa.fa_fwd_splitkv_plan(1, 32, 16384, 128, 1)[0] == 1      # 2048 blocks fill the GPU
-    assert fa.fa_fwd_splitkv_plan(1, 1, 256, 64, 0)[0] == 4          # one block, four 64-key tiles
+    assert fa.fa_fwd_splitkv_plan(1, 1, 256, 64, 0)[0] == 1          # four 64-key tiles: too short to split
+    assert fa.fa_fwd_splitkv_plan(1, 1, 4096, 64, 0)[0] == 8         # 64 tiles: 8 ranges of 8
     with pytest.raises(fa.FaError):
         fa.fa_fwd_splitkv_plan(1, 1, 16, 96, 0)
 

@@ -145,6 +145,25 @@ def fa_fwd_tile(B, H, N, d, causal):
     return r.value, c.value, w.value, g.value
 
 
+def _check_inputs(ts, names, device):
+    """Every input on `device` (the first input's) and contiguous."""
+    for t, name in zip(ts, names):
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be a GPU tensor on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _check_buffer(t, name, dtype, shape, device):
+    """A caller-provided output or workspace: the library writes it through a
+    raw pointer, so its dtype, exact shape, device and layout are checked
+    here before any launch."""
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
 def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """Attention forward on torch tensors: returns (o, lse).
 
@@ -159,15 +178,16 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
         raise ValueError("q, k, v must be GPU tensors")
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    _check_inputs((q, k, v), ("q", "k", "v"), q.device)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer(out, "out", torch.bfloat16, q.shape, q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_buffer(lse, "lse", torch.float32, (B, H, N), q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -193,16 +213,16 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
         raise ValueError("all tensors must be GPU tensors")
     if q.dim() != 4 or any(t.shape != q.shape for t in ts) or lse.shape != q.shape[:3]:
         raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape and lse be [B, H, N]")
-    if not all(t.is_contiguous() for t in ts + (lse,)):
-        raise ValueError("all tensors must be contiguous")
+    _check_inputs(ts + (lse,), ("q", "k", "v", "o", "dout", "lse"), q.device)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dq = _check_buffer(torch.empty_like(q) if dq is None else dq, "dq", torch.bfloat16, q.shape, q.device)
+    dk = _check_buffer(torch.empty_like(q) if dk is None else dk, "dk", torch.bfloat16, q.shape, q.device)
+    dv = _check_buffer(torch.empty_like(q) if dv is None else dv, "dv", torch.bfloat16, q.shape, q.device)
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_buffer(delta, "delta", torch.float32, (B, H, N), q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
@@ -228,20 +248,20 @@ def fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=None, out=None, lse=
         raise ValueError("q, k, v must be GPU tensors")
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    _check_inputs((q, k, v), ("q", "k", "v"), q.device)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if n_splits is None:
         n_splits = fa_fwd_splitkv_plan(B, H, N, d, causal)[0]
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if o_part is None:
-        o_part = torch.empty((n_splits, B, H, N, d), dtype=torch.float32, device=q.device)
-    if lse_part is None:
-        lse_part = torch.empty((n_splits, B, H, N), dtype=torch.float32, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = _check_buffer(torch.empty_like(q) if out is None else out, "out", torch.bfloat16, q.shape, q.device)
+    lse = _check_buffer(torch.empty((B, H, N), **f32) if lse is None else lse, "lse", torch.float32,
+                        (B, H, N), q.device)
+    o_part = _check_buffer(torch.empty((n_splits, B, H, N, d), **f32) if o_part is None else o_part, "o_part",
+                           torch.float32, (n_splits, B, H, N, d), q.device)
+    lse_part = _check_buffer(torch.empty((n_splits, B, H, N), **f32) if lse_part is None else lse_part,
+                             "lse_part", torch.float32, (n_splits, B, H, N), q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
@@ -261,17 +281,18 @@ def fwd_fa1order(q, k, v, scale=None, causal=False, out=None, lse=None, o_acc=No
         raise TypeError("q, k, v must be bfloat16")
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+    _check_inputs((q, k, v), ("q", "k", "v"), q.device)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out = torch.empty_like(q) if out is None else out
     f32 = dict(dtype=torch.float32, device=q.device)
-    lse = torch.empty((B, H, N), **f32) if lse is None else lse
-    o_acc = torch.empty((B, H, N, d), **f32) if o_acc is None else o_acc
-    m = torch.empty((B, H, N), **f32) if m is None else m
-    l = torch.empty((B, H, N), **f32) if l is None else l
+    out = _check_buffer(torch.empty_like(q) if out is None else out, "out", torch.bfloat16, q.shape, q.device)
+    lse = _check_buffer(torch.empty((B, H, N), **f32) if lse is None else lse, "lse", torch.float32,
+                        (B, H, N), q.device)
+    o_acc = _check_buffer(torch.empty((B, H, N, d), **f32) if o_acc is None else o_acc, "o_acc", torch.float32,
+                          (B, H, N, d), q.device)
+    m = _check_buffer(torch.empty((B, H, N), **f32) if m is None else m, "m", torch.float32, (B, H, N), q.device)
+    l = _check_buffer(torch.empty((B, H, N), **f32) if l is None else l, "l", torch.float32, (B, H, N), q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_fa1order(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
@@ -292,7 +313,9 @@ def quant_fp8(x, rotate=False, sign_bits=0, out=None, descale=None, stream=None)
         raise ValueError("x must be a contiguous bf16 GPU tensor [B, H, N, d]")
     B, H, N, d = x.shape
     out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    _check_buffer(out, "out", torch.uint8, x.shape, x.device)
     descale = torch.empty((B, H), dtype=torch.float32, device=x.device) if descale is None else descale
+    _check_buffer(descale, "descale", torch.float32, (B, H), x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     bits = int(sign_bits)
@@ -314,16 +337,18 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, scale=None, causal=Fals
     q8, k8, v8 = t8
     if q8.dim() != 4 or q8.shape != k8.shape or q8.shape != v8.shape:
         raise ValueError("q8, k8, v8 must share one [B, H, N, d] shape")
-    if not (q8.is_contiguous() and k8.is_contiguous() and v8.is_contiguous()):
-        raise ValueError("q8, k8, v8 must be contiguous")
+    _check_inputs((q8, k8, v8, q_descale, k_descale, v_descale),
+                  ("q8", "k8", "v8", "q_descale", "k_descale", "v_descale"), q8.device)
     B, H, N, d = q8.shape
     for t in (q_descale, k_descale, v_descale):
-        if t.dtype != torch.float32 or t.numel() != B * H or not t.is_contiguous():
+        if t.dtype != torch.float32 or t.numel() != B * H:
             raise ValueError("descale factors must be contiguous fp32 [B, H]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    _check_buffer(out, "out", torch.bfloat16, q8.shape, q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _check_buffer(lse, "lse", torch.float32, (B, H, N), q8.device)
     if stream is None:
         stream = torch.cuda.current_stream(q8.device)
     st = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),

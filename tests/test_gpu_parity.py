@@ -182,3 +182,48 @@ def test_late_dominant_key_moves_the_reference(d):
         announce(f"[late key d={d} scale {scale:.3f}] max|dO|={raw:.3e} (beyond O's rounding {beyond:.3e}) "
                  f"mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
         assert beyond <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+
+
+def test_caller_buffers_of_the_wrong_shape_dtype_or_layout_are_rejected():
+    """Outputs and workspaces the caller passes reach the kernels as raw
+    pointers; a buffer that does not match is refused before any launch and
+    is left untouched."""
+    dev = device()
+    w = workloads.custom(1, 2, 300, 64, True, seed=21)
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    B, H, N, d = q.shape
+    short_o = torch.full((B, H, N - 1, d), 3.0, dtype=torch.bfloat16, device=dev)
+    f32_o = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+    strided_o = torch.zeros((B, H, d, N), dtype=torch.bfloat16, device=dev).transpose(2, 3)
+    short_l = torch.full((B, H, N - 1), 3.0, dtype=torch.float32, device=dev)
+    for kw in ({"out": short_o}, {"out": f32_o}, {"out": strided_o}, {"lse": short_l}):
+        with pytest.raises(ValueError):
+            fa.fwd(q, k, v, causal=True, **kw)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dout = torch.randn_like(o)
+    for name in ("dq", "dk", "dv"):
+        with pytest.raises(ValueError):
+            fa.bwd(q, k, v, o, lse, dout, causal=True, **{name: short_o})
+    with pytest.raises(ValueError):
+        fa.bwd(q, k, v, o, lse, dout, causal=True, delta=short_l)
+    with pytest.raises(ValueError):
+        fa.fwd_splitkv(q, k, v, causal=True, n_splits=2,
+                       o_part=torch.empty((1, B, H, N, d), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        fa.fwd_splitkv(q, k, v, causal=True, n_splits=2,
+                       lse_part=torch.empty((2, B, H, N - 1), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        fa.fwd_fa1order(q, k, v, causal=True, o_acc=torch.empty(q.shape, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        fa.fwd_fa1order(q, k, v, causal=True, m=short_l)
+    with pytest.raises(ValueError):
+        fa.quant_fp8(q, out=torch.empty((B, H, N - 1, d), dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):
+        fa.quant_fp8(q, descale=torch.empty((B, H + 1), dtype=torch.float32, device=dev))
+    q8, qd = fa.quant_fp8(q)
+    with pytest.raises(ValueError):
+        fa.fwd_fp8(q8, q8, q8, qd, qd, qd, causal=True, out=short_o)
+    with pytest.raises(ValueError):
+        fa.fwd(q, k.cpu(), v, causal=True)
+    torch.cuda.synchronize()
+    assert (short_o == 3.0).all().item() and (short_l == 3.0).all().item()

@@ -52,7 +52,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # (workload, pass): (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     ("causal_b1h32_n16384_d128", "fwd"): (
-        "05913340d5eb92cac8115d51a9ecdd1daf54cc3750d2f8425458901c7d116856", 3.48992e5, 1.33120e5),
+        "7dcaa7c7d3f18ce93ee5467007b0466be6afa6dd168da383f4b6e320ab9eb093", 3.48538e5, 1.33120e5),
     ("causal_b1h32_n16384_d128", "fwd_fp8"): (
         "abe8d17c666a0d56fb8c12b9825471c41b185aa064b8e840237156406444970d", 1.54652e5, 1.33154e5),
 }
@@ -362,7 +362,10 @@ def main():
                    "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
                    **({"pct_of_fp8_peak": round(100 * value / peak, 2), "quantisation": quant} if args.fp8 else {}),
                    "launch": {"rows_per_block": rows, "keys_per_tile": keys, "waves": waves,
-                              "blocks": blocks}},
+                              "blocks": blocks},
+                   "launch_ms": {"mean": round(avg_launch_ms, 5), "median": round(per[len(per) // 2], 5),
+                                 "min": round(per[0], 5)},
+                   "tflops_at_median_launch": round(flops / (per[len(per) // 2] * 1e-3) / 1e12, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),

@@ -84,8 +84,8 @@ template <int D> constexpr int kThreadsOf = kWavesOf<D> * 64;
 template <int D> constexpr int kBROf = kWavesOf<D> * 32;   // query rows per workgroup
 __host__ __device__ constexpr int rows_per_block(int d) { return d == 64 ? kBROf<64> : kBROf<128>; }
 __host__ __device__ constexpr int threads_per_block(int d) { return d == 64 ? kThreadsOf<64> : kThreadsOf<128>; }
-constexpr int kXcds = 8;
-constexpr int kMaxSplits = 64;    // key ranges per query block in the split-KV forward          // accelerator dies; workgroups are dealt to them round-robin
+constexpr int kXcds = 8;          // accelerator dies; workgroups are dealt to them round-robin
+constexpr int kMaxSplits = 64;    // key ranges per query block in the split-KV forward
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kPMax = 4294967296.0f;   // 2^32: largest tile sum of P a lane may reach before the reference moves

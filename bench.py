@@ -7,7 +7,7 @@ roofline fraction of the dominant (only) kernel against the bf16 dense MFMA
 peak, and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--all] [--shape B,H,N,d,causal]
+                       [--no-cpu-baseline] [--all] [--shape B,H,N,d,causal] [--warm-s S]
 
 --splitkv S measures fa_fwd_splitkv with S key ranges per query block (-1:
 the library's plan) instead of fa_fwd.
@@ -38,6 +38,12 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOPS & % of MI355X bf16 MFMA peak at N=16K,d=128 (1 GPU)"
 METRIC_BWD = "attention bwd TFLOPS (5 products, 2.5x fwd FLOPs) & % of MI355X bf16 MFMA peak (1 GPU)"
 METRIC_FP8 = "attention fwd FP8 (E4M3) TFLOPS & % of MI355X fp8 MFMA peak at N=16K,d=128 (1 GPU)"
+
+# --all: each extra workload is timed over ALL_STEPS calls after ALL_WARM_S
+# seconds of untimed calls (its inputs are made on the host first, during
+# which the GPU idles and its clock drops)
+ALL_STEPS = 20
+ALL_WARM_S = 0.3
 
 KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "fwd_fp8": "fa_fp8.hip"}
 
@@ -96,10 +102,13 @@ def log_sclk(when):
         log(f"[bench] sclk {when}: unreadable ({e.strerror})")
 
 
-def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, fp8=False):
+def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, fp8=False, warm_s=0.0):
     """Time `steps` calls of the forward (or, with backward, of fa_bwd on the
     forward's outputs) with HIP events on the launch stream: returns the total
-    of the timed region and the sorted per-call durations, in ms."""
+    of the timed region and the sorted per-call durations, in ms.  After the
+    `warmup` calls, untimed calls continue until `warm_s` seconds have passed
+    (0: none), so that the shader clock has left its idle level before a
+    short workload is timed."""
     import torch
     import io_aware_exact_13_amd as fa
     import workloads
@@ -147,6 +156,11 @@ def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, 
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < warm_s:
+        for _ in range(4):
+            call()
+        torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -250,6 +264,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-s", type=float, default=0.0,
+                    help="after the warmup calls, keep calling (untimed) for this many seconds")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
     ap.add_argument("--shape", default=None, help="B,H,N,d,causal instead of a named workload")
     ap.add_argument("--bwd", action="store_true", help="measure fa_bwd (the gradients) instead of the forward")
@@ -297,7 +313,8 @@ def main():
     if args.splitkv < 0:
         args.splitkv = fa.fa_fwd_splitkv_plan(w.B, w.H, w.N, w.d, int(w.causal))[0]
     total_ms, per = time_workload(w, args.steps, args.warmup, backward=args.bwd,
-                                  n_splits=0 if args.bwd else args.splitkv, fa1order=args.fa1order, fp8=args.fp8)
+                                  n_splits=0 if args.bwd else args.splitkv, fa1order=args.fa1order, fp8=args.fp8,
+                                  warm_s=args.warm_s)
     log_sclk("after")
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -322,9 +339,9 @@ def main():
             other = ow.name
             for mode in ("fwd", "bwd", "fp8"):
                 bw = mode == "bwd"
-                tms, p = time_workload(ow, max(5, args.steps // 2), 3, backward=bw, fp8=mode == "fp8")
+                tms, p = time_workload(ow, ALL_STEPS, 3, backward=bw, fp8=mode == "fp8", warm_s=ALL_WARM_S)
                 f = (acc.attention_bwd_flops if bw else acc.attention_flops)(ow.B, ow.H, ow.N, ow.d, ow.causal)
-                t = tms / max(5, args.steps // 2)
+                t = tms / ALL_STEPS
                 pk = acc.PEAK_FP8_DENSE_TFLOPS if mode == "fp8" else acc.PEAK_BF16_DENSE_TFLOPS
                 log(f"[bench-all] {other:32s} {mode} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s "
@@ -335,8 +352,8 @@ def main():
             plan = fa.fa_fwd_splitkv_plan(sw.B, sw.H, sw.N, sw.d, int(sw.causal))[0]
             f = acc.attention_flops(sw.B, sw.H, sw.N, sw.d, sw.causal)
             for ns in sorted({0, 2, plan, 8}):
-                tms, p = time_workload(sw, max(5, args.steps // 2), 3, n_splits=ns)
-                t = tms / max(5, args.steps // 2)
+                tms, p = time_workload(sw, ALL_STEPS, 3, n_splits=ns, warm_s=ALL_WARM_S)
+                t = tms / ALL_STEPS
                 log(f"[bench-all] {sw.name:32s} {'fwd' if ns == 0 else f'split{ns}':>7s} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s{'  (plan)' if ns == plan else ''}")
 
@@ -359,6 +376,7 @@ def main():
                    "pass": "bwd" if args.bwd else ("fwd_fa1order" if args.fa1order else "fwd_fp8" if args.fp8 else
                                                    (f"fwd_splitkv{args.splitkv}" if args.splitkv else "fwd")), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "seed": w.seed,
+                   **({"untimed_warm_s": args.warm_s} if args.warm_s else {}),
                    "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
                    **({"pct_of_fp8_peak": round(100 * value / peak, 2), "quantisation": quant} if args.fp8 else {}),
                    "launch": {"rows_per_block": rows, "keys_per_tile": keys, "waves": waves,

@@ -8,7 +8,11 @@ peak, and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--all] [--shape B,H,N,d,causal] [--warm-s S]
+                       [--input-bits normal|coarse|const]
 
+--input-bits is a power diagnostic: the same launch on inputs whose low
+mantissa bits are cleared (coarse) or that are all 0.5 (const); the line's
+"data" field says so, and its value is not the workload's throughput.
 --splitkv S measures fa_fwd_splitkv with S key ranges per query block (-1:
 the library's plan) instead of fa_fwd.
 --fa1order measures the K/V-outer loop-order ablation fa_fwd_fa1order.
@@ -102,7 +106,21 @@ def log_sclk(when):
         log(f"[bench] sclk {when}: unreadable ({e.strerror})")
 
 
-def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, fp8=False, warm_s=0.0):
+def diagnostic_inputs(tensors, bits):
+    """Power diagnostic: the workload's bf16 inputs with their low 5 mantissa
+    bits cleared ("coarse") or every element 0.5 ("const"); "normal" leaves
+    them unchanged.  Same shapes, launch and instruction stream; only the bits
+    the datapaths move change."""
+    import torch
+    if bits == "coarse":
+        return [(t.view(torch.int16) & ~0x1F).view(torch.bfloat16) for t in tensors]
+    if bits == "const":
+        return [torch.full_like(t, 0.5) for t in tensors]
+    return list(tensors)
+
+
+def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, fp8=False, warm_s=0.0,
+                  input_bits="normal"):
     """Time `steps` calls of the forward (or, with backward, of fa_bwd on the
     forward's outputs) with HIP events on the launch stream: returns the total
     of the timed region and the sorted per-call durations, in ms.  After the
@@ -114,7 +132,7 @@ def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, 
     import workloads
 
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    q, k, v = (t.to(dev) for t in diagnostic_inputs(workloads.make_inputs(w), input_bits))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -264,6 +282,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--input-bits", choices=("normal", "coarse", "const"), default="normal",
+                    help="power diagnostic: clear the inputs' low mantissa bits or make them constant")
     ap.add_argument("--warm-s", type=float, default=0.0,
                     help="after the warmup calls, keep calling (untimed) for this many seconds")
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr table)")
@@ -314,7 +334,7 @@ def main():
         args.splitkv = fa.fa_fwd_splitkv_plan(w.B, w.H, w.N, w.d, int(w.causal))[0]
     total_ms, per = time_workload(w, args.steps, args.warmup, backward=args.bwd,
                                   n_splits=0 if args.bwd else args.splitkv, fa1order=args.fa1order, fp8=args.fp8,
-                                  warm_s=args.warm_s)
+                                  warm_s=args.warm_s, input_bits=args.input_bits)
     log_sclk("after")
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -371,7 +391,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3" if args.fp8 else "bf16",
-        "data": "synthetic",
+        "data": ("synthetic" if args.input_bits == "normal" else
+                 f"synthetic, power diagnostic: inputs '{args.input_bits}' (not the workload's values)"),
         "config": {"workload": name,
                    "pass": "bwd" if args.bwd else ("fwd_fa1order" if args.fa1order else "fwd_fp8" if args.fp8 else
                                                    (f"fwd_splitkv{args.splitkv}" if args.splitkv else "fwd")), "B": w.B, "H": w.H, "N": w.N, "d": w.d,

@@ -62,7 +62,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # (workload, pass): (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     ("causal_b1h32_n16384_d128", "fwd"): (
-        "7dcaa7c7d3f18ce93ee5467007b0466be6afa6dd168da383f4b6e320ab9eb093", 3.48538e5, 1.33120e5),
+        "595b2c912dc4b7e26b040d82b025c83d2ad49d4db6b1ccae59c3029ad3ffd455", 3.39127e5, 1.33120e5),
     ("causal_b1h32_n16384_d128", "fwd_fp8"): (
         "abe8d17c666a0d56fb8c12b9825471c41b185aa064b8e840237156406444970d", 1.54652e5, 1.33154e5),
 }

@@ -72,6 +72,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
@@ -678,14 +679,21 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
     return;
   }
-  if (qrow < N) {
-    const float inv = 1.0f / l_tot;
-    __bf16* orow = O + head_off + (size_t)qrow * D;
+  // O = acc / l in bf16, staged through this wave's 32-row slice of the K
+  // ring (idle since the barrier above: every K read and copy has finished)
+  // so that the stores to HBM are whole rows, 16 bytes a lane: a lane's own
+  // accumulators hold 8-byte pieces of one row, which stored directly touch
+  // 32 rows per instruction.  Chunk ch of staged row r sits at 16-byte slot
+  // ch ^ (r % kChunks) of the row, so the 32 rows written by one instruction
+  // spread over the banks.
+  {
+    constexpr int kChunks = G::kChunks;
+    char* stage = lds + G::k_buf(0) + c.wave * 32 * G::kRowBytes;
+    const float inv = qrow < N ? 1.0f / l_tot : 0.f;
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int c0 = ct * 32 + r4 * 8 + c.h * 4;
         const __bf16 b0 = (__bf16)(st.acc[ct][r4 * 4 + 0] * inv);
         const __bf16 b1 = (__bf16)(st.acc[ct][r4 * 4 + 1] * inv);
         const __bf16 b2 = (__bf16)(st.acc[ct][r4 * 4 + 2] * inv);
@@ -693,8 +701,21 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         u32x2 w;
         w[0] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
         w[1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *reinterpret_cast<u32x2*>(orow + c0) = w;
+        // columns ct*32 + r4*8 + 4h .. +3: chunk 4ct + r4, half h
+        const int ch = ct * 4 + r4;
+        *reinterpret_cast<u32x2*>(stage + l32 * G::kRowBytes + ((ch ^ (l32 % kChunks)) << 4) + 8 * c.h) = w;
       }
+    // the wave reads back what its other lanes wrote: wait for the writes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int row0 = q0 + c.wave * 32;
+#pragma unroll
+    for (int i = 0; i < kChunks / 2; ++i) {
+      const int q = i * 64 + lane, r = q / kChunks, ch = q % kChunks;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * G::kRowBytes + ((ch ^ (r % kChunks)) << 4));
+      if (row0 + r < N) *reinterpret_cast<u32x4*>(O + head_off + (size_t)(row0 + r) * D + ch * 8) = val;
+    }
+  }
+  if (qrow < N) {
     if (c.h == 0) LSE[(size_t)bh * N + qrow] = (st.m_ref + log2f(l_tot)) * kLn2;
   }
 }
@@ -735,7 +756,6 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
     packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1) << 16);
   }
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   *reinterpret_cast<u32x4*>(O + row * D + c0) = u32x4{packed[0], packed[1], packed[2], packed[3]};
   if (c0 == 0) LSE[row] = m + log2f(z) * kLn2;
 }

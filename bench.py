@@ -64,7 +64,7 @@ MEASURED_TRAFFIC = {
     ("causal_b1h32_n16384_d128", "fwd"): (
         "595b2c912dc4b7e26b040d82b025c83d2ad49d4db6b1ccae59c3029ad3ffd455", 3.39127e5, 1.33120e5),
     ("causal_b1h32_n16384_d128", "fwd_fp8"): (
-        "abe8d17c666a0d56fb8c12b9825471c41b185aa064b8e840237156406444970d", 1.54652e5, 1.33154e5),
+        "deb0c661177148065729940e4d3f5a9e647df350effa3e6c234ee8590f294520", 1.54121e5, 1.33120e5),
 }
 
 

@@ -447,14 +447,21 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
   }
 
   const float l_tot = sum_halves(st.l_part);
-  if (qrow < N) {
-    const float inv = dv / l_tot;
-    __bf16* orow = O + head_off + (size_t)qrow * D;
+  // O = acc * dv / l in bf16, staged through this wave's slice of the K ring
+  // (idle since the barrier above) and stored as whole rows, 16 bytes a lane,
+  // as in the bf16 forward: chunk ch of staged row r sits at slot
+  // ch ^ (r % kOutChunks).  Four waves of 32 rows of 2D bytes fill the ring
+  // exactly.
+  {
+    constexpr int kOutRow = 2 * D;                  // bytes of one bf16 output row
+    constexpr int kOutChunks = kOutRow / 16;
+    static_assert(kWaves * 32 * kOutRow <= G::kRing * G::kTile, "staging fits the K ring");
+    char* stage = lds + G::k_buf(0) + c.wave * 32 * kOutRow;
+    const float inv = qrow < N ? dv / l_tot : 0.f;
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int c0 = ct * 32 + r4 * 8 + c.h * 4;
         const __bf16 b0 = (__bf16)(st.acc[ct][r4 * 4 + 0] * inv);
         const __bf16 b1 = (__bf16)(st.acc[ct][r4 * 4 + 1] * inv);
         const __bf16 b2 = (__bf16)(st.acc[ct][r4 * 4 + 2] * inv);
@@ -462,10 +469,21 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
         u32x2 w;
         w[0] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
         w[1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *reinterpret_cast<u32x2*>(orow + c0) = w;
+        // columns ct*32 + r4*8 + 4h .. +3: chunk 4ct + r4, half h
+        const int ch = ct * 4 + r4;
+        *reinterpret_cast<u32x2*>(stage + l32 * kOutRow + ((ch ^ (l32 % kOutChunks)) << 4) + 8 * c.h) = w;
       }
-    if (c.h == 0) LSE[(size_t)bh * N + qrow] = (st.m_ref + log2f(l_tot)) * kLn2;
+    // the wave reads back what its other lanes wrote: wait for the writes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int row0 = q0 + c.wave * 32;
+#pragma unroll
+    for (int i = 0; i < kOutChunks / 2; ++i) {
+      const int q = i * 64 + lane, r = q / kOutChunks, ch = q % kOutChunks;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * kOutRow + ((ch ^ (r % kOutChunks)) << 4));
+      if (row0 + r < N) *reinterpret_cast<u32x4*>(O + head_off + (size_t)(row0 + r) * D + ch * 8) = val;
+    }
   }
+  if (qrow < N && c.h == 0) LSE[(size_t)bh * N + qrow] = (st.m_ref + log2f(l_tot)) * kLn2;
 }
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);

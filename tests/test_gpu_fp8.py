@@ -242,6 +242,31 @@ def test_fp8_is_bitwise_deterministic():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 3, 777, 128, True), (1, 2, 333, 64, False)])
+def test_fp8_writes_nothing_outside_its_outputs(B, H, N, d, causal):
+    """Canary bytes around O and LSE stay untouched on ragged heads (the last
+    query block's rows past N are staged but never stored)."""
+    dev = device()
+    w = workloads.custom(B, H, N, d, causal, seed=6500 + N)
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    signs = workloads.make_fp8_signs(w.seed, d)
+    (q8, qd), (k8, kd), (v8, vd) = (fa.quant_fp8(q, rotate=True, sign_bits=signs),
+                                    fa.quant_fp8(k, rotate=True, sign_bits=signs), fa.quant_fp8(v))
+    announce(f"[fp8-canary] {w.name}")
+    n_o, n_l, pad = q.numel(), B * H * N, 4096
+    o_buf = torch.full((n_o + 2 * pad,), -7.25, dtype=torch.bfloat16, device=dev)
+    l_buf = torch.full((n_l + 2 * pad,), -7.25, dtype=torch.float32, device=dev)
+    o = o_buf[pad:pad + n_o].view(q.shape)
+    lse = l_buf[pad:pad + n_l].view(B, H, N)
+    fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=causal, out=o, lse=lse)
+    o2, l2 = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), l2.view(torch.int32))
+    for buf in (o_buf, l_buf):
+        assert (buf[:pad] == -7.25).all().item() and (buf[-pad:] == -7.25).all().item()
+
+
 def test_rotation_lowers_the_fp8_error_end_to_end():
     """Whole GPU path (quantise + forward) against the fp64 attention of the
     bf16 inputs, on inputs with two outlier channels shared by Q and K: the

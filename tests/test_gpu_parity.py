@@ -97,9 +97,11 @@ def test_closed_forms_on_gpu():
     assert torch.equal(o.cpu().view(torch.int16), v.view(torch.int16))
 
 
-def test_bitwise_deterministic_and_no_out_of_bounds_writes():
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 4, 777, 128, True), (1, 3, 333, 64, False)])
+def test_bitwise_deterministic_and_no_out_of_bounds_writes(B, H, N, d, causal):
     dev = device()
-    w = workloads.custom(2, 4, 777, 128, True, seed=9)
+    w = workloads.custom(B, H, N, d, causal, seed=9)
+    announce(f"[canary] {w.name}")
     q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
     n_o, n_l = q.numel(), w.B * w.H * w.N
     pad = 4096
@@ -107,8 +109,8 @@ def test_bitwise_deterministic_and_no_out_of_bounds_writes():
     l_buf = torch.full((n_l + 2 * pad,), -7.25, dtype=torch.float32, device=dev)
     o = o_buf[pad:pad + n_o].view(q.shape)
     lse = l_buf[pad:pad + n_l].view(w.B, w.H, w.N)
-    fa.fwd(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
-    o2, l2 = fa.fwd(q, k, v, scale=w.scale, causal=True)
+    fa.fwd(q, k, v, scale=w.scale, causal=causal, out=o, lse=lse)
+    o2, l2 = fa.fwd(q, k, v, scale=w.scale, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), l2.view(torch.int32))

@@ -40,6 +40,28 @@ def test_small_shapes_match_oracle_everywhere(B, H, N, d, causal):
     assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
 
 
+def _random_shapes(seed, count):
+    """Seeded ragged shapes away from the tile multiples the fixed list favours."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        N = int(rng.integers(1, 1600))
+        out.append((B, H, N, int(rng.choice([64, 128])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", _random_shapes(20261203, 16))
+def test_random_shapes_match_oracle_everywhere(B, H, N, d, causal):
+    w = workloads.custom(B, H, N, d, causal, seed=5000 + N)
+    q, k, v = workloads.make_inputs(w)
+    announce(f"[parity-random] {w.name}")
+    o, lse = run_gpu(q, k, v, w.scale, causal)
+    mo, me, ml = compare_full(q, k, v, w.scale, causal, o, lse)
+    announce(f"    max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+
+
 def test_tiny_workload_full_compare():
     w = workloads.WORKLOADS["tiny_b1h1_n256_d64"]
     q, k, v = workloads.make_inputs(w)

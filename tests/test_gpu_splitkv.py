@@ -29,7 +29,14 @@ def run_split(q, k, v, scale, causal, n_splits):
     return o, lse
 
 
-@pytest.mark.parametrize("B,H,N,d,causal,n_splits", CASES)
+def _random_cases(seed, count):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 1600)),
+             int(rng.choice([64, 128])), bool(rng.integers(0, 2)), int(rng.integers(1, 9)))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,n_splits", CASES + _random_cases(20261204, 8))
 def test_small_shapes_match_oracle(B, H, N, d, causal, n_splits):
     w = workloads.custom(B, H, N, d, causal, seed=3000 + N + d + n_splits)
     q, k, v = workloads.make_inputs(w)

@@ -62,7 +62,7 @@ WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # (workload, pass): (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     ("causal_b1h32_n16384_d128", "fwd"): (
-        "595b2c912dc4b7e26b040d82b025c83d2ad49d4db6b1ccae59c3029ad3ffd455", 3.39127e5, 1.33120e5),
+        "3c3dd51a4d12e301fbfa52def76744292e22ff2a73f80a9b8c4f3ac9b503dad8", 3.35861e5, 1.33120e5),
     ("causal_b1h32_n16384_d128", "fwd_fp8"): (
         "deb0c661177148065729940e4d3f5a9e647df350effa3e6c234ee8590f294520", 1.54121e5, 1.33120e5),
 }

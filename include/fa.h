@@ -115,8 +115,9 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * fa_fwd_splitkv_plan -- a split count for (B, H, N, d, causal) that gives
- * about two workgroups per compute unit (1 when fa_fwd alone does, or when
- * the ranges would hold fewer than 8 key tiles of 64), at most 16, and the
+ * about two rounds of the workgroups the GPU runs at once (one per compute
+ * unit at d = 128, two at d = 64; 1 when fa_fwd alone fills two rounds, or
+ * when the ranges would hold fewer than 8 key tiles of 64), at most 16, and the
  * workspace bytes fa_fwd_splitkv needs for it.  Any output pointer may be
  * NULL.  Returns FA_OK or the FA_ERR_* code fa_fwd would return.  Host only.
  */

@@ -852,13 +852,15 @@ extern "C" int fa_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int* 
   long long blocks = 0;
   const int st = check_shape(B, H, N, d, causal, &blocks);
   if (st != FA_OK) return st;
-  // enough workgroups for two per CU (256 CUs), at least 8 key tiles per
-  // range of the longest query block (shorter ranges do not pay for the
+  // enough workgroups for two rounds of the ones the GPU holds at once (256
+  // CUs, one workgroup each at d = 128, two at d = 64), at least 8 key tiles
+  // per range of the longest query block (shorter ranges do not pay for the
   // merge launch), at most 16.  More splits balance the causal block lengths
   // better but cost the fp32 partials' round trip through HBM
   // (2 n_splits B H N d 4 bytes).
   const long long tiles = ((long long)N + kBC - 1) / kBC;
-  long long n = (2LL * 256 + blocks - 1) / blocks;
+  const long long resident = 256LL * (d == 64 ? 2 : 1);
+  long long n = (2 * resident + blocks - 1) / blocks;
   n = max(1LL, min(n, min(16LL, tiles / 8)));
   if (n_splits) *n_splits = (int)n;
   const size_t rows = (size_t)B * H * (size_t)N;

@@ -140,6 +140,8 @@ def test_splitkv_plan(lib):
     assert fa.fa_fwd_splitkv_plan(1, 32, 16384, 128, 1)[0] == 1      # 2048 blocks fill the GPU
     assert fa.fa_fwd_splitkv_plan(1, 1, 256, 64, 0)[0] == 1          # four 64-key tiles: too short to split
     assert fa.fa_fwd_splitkv_plan(1, 1, 4096, 64, 0)[0] == 8         # 64 tiles: 8 ranges of 8
+    assert fa.fa_fwd_splitkv_plan(1, 4, 16384, 64, 1)[0] == 2        # 512 blocks, two resident per CU
+    assert fa.fa_fwd_splitkv_plan(1, 2, 16384, 128, 1)[0] == 4       # 128 blocks
     with pytest.raises(fa.FaError):
         fa.fa_fwd_splitkv_plan(1, 1, 16, 96, 0)
 

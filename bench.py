@@ -8,11 +8,13 @@ peak, and the CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--all] [--shape B,H,N,d,causal] [--warm-s S]
-                       [--input-bits normal|coarse|const]
+                       [--input-bits normal|coarse|const] [--lib PATH]
 
 --input-bits is a power diagnostic: the same launch on inputs whose low
 mantissa bits are cleared (coarse) or that are all 0.5 (const); the line's
 "data" field says so, and its value is not the workload's throughput.
+--lib times another build of the library: a tile candidate of the forward
+made by `python -m io_aware_exact_13_amd.build --tile-variant NAME`.
 --splitkv S measures fa_fwd_splitkv with S key ranges per query block (-1:
 the library's plan) instead of fa_fwd.
 --fa1order measures the K/V-outer loop-order ablation fa_fwd_fa1order.
@@ -56,13 +58,14 @@ KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "fwd_fp8": "fa_fp8.hip"}
 # counter reads for a plain 512 MiB device copy (FETCH_SIZE reads half of the
 # bytes the copy moves, WRITE_SIZE all of them).  Keyed by workload and pass;
 # each entry records the sha256 of the kernel source the counters were taken
-# on, and is reported only while that source is unchanged.
+# on (or of a later source shown to compile to the same kernel code), and is
+# reported only while that source is unchanged.
 FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # (workload, pass): (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
     ("causal_b1h32_n16384_d128", "fwd"): (
-        "3c3dd51a4d12e301fbfa52def76744292e22ff2a73f80a9b8c4f3ac9b503dad8", 3.35861e5, 1.33120e5),
+        "d03e47be951252f44ac3469b435e7c4f3635315c124d38ed61cab95baa1af45b", 3.35861e5, 1.33120e5),
     ("causal_b1h32_n16384_d128", "fwd_fp8"): (
         "deb0c661177148065729940e4d3f5a9e647df350effa3e6c234ee8590f294520", 1.54121e5, 1.33120e5),
 }
@@ -282,6 +285,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lib", default=None,
+                    help="time this build of the library (a tile candidate from build.py --tile-variant)")
     ap.add_argument("--input-bits", choices=("normal", "coarse", "const"), default="normal",
                     help="power diagnostic: clear the inputs' low mantissa bits or make them constant")
     ap.add_argument("--warm-s", type=float, default=0.0,
@@ -306,6 +311,8 @@ def main():
     import workloads
     from io_aware_exact_13_amd import accounting as acc
 
+    if args.lib:
+        fa.use_library(args.lib)
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -377,7 +384,7 @@ def main():
                 log(f"[bench-all] {sw.name:32s} {'fwd' if ns == 0 else f'split{ns}':>7s} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s{'  (plan)' if ns == plan else ''}")
 
-    traffic = (None if (args.bwd or args.splitkv or args.fa1order) else
+    traffic = (None if (args.bwd or args.splitkv or args.fa1order or args.lib) else
                measured_traffic(name, "fwd_fp8" if args.fp8 else "fwd"))
     result = {
         "metric": METRIC_BWD if args.bwd else (METRIC_FP8 if args.fp8 else METRIC),
@@ -398,6 +405,7 @@ def main():
                                                    (f"fwd_splitkv{args.splitkv}" if args.splitkv else "fwd")), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "seed": w.seed,
                    **({"untimed_warm_s": args.warm_s} if args.warm_s else {}),
+                   **({"library": os.path.basename(args.lib)} if args.lib else {}),
                    "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
                    **({"pct_of_fp8_peak": round(100 * value / peak, 2), "quantisation": quant} if args.fp8 else {}),
                    "launch": {"rows_per_block": rows, "keys_per_tile": keys, "waves": waves,

@@ -33,12 +33,25 @@ class FaError(RuntimeError):
         self.status = status
 
 
+_lib_override = None
+
+
+def use_library(path: str) -> None:
+    """Load the HIP library from `path` instead of the default build (for
+    timing a tile candidate built by build.py --tile-variant).  Must be called
+    before the first call into the library."""
+    global _lib_override
+    if _lib is not None:
+        raise RuntimeError("the HIP library is already loaded")
+    _lib_override = os.path.abspath(path)
+
+
 def load_library():
     """Load the built HIP library (raises if it is missing)."""
     global _lib
     if _lib is not None:
         return _lib
-    path = lib_path()
+    path = _lib_override or lib_path()
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() "
                            "or python -m io_aware_exact_13_amd.build")

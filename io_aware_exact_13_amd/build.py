@@ -20,14 +20,27 @@ FLAGS = [
 ]
 
 
-def lib_path() -> str:
-    return os.path.join(PKG, LIB_NAME)
+# Tile candidates of the bf16 forward, for measurement only: each overrides
+# compile-time constants of fa_fwd.hip (the default build overrides none).
+TILE_VARIANTS = {
+    "w4d128": ["-DFA_WAVES_D128=4"],       # 4 waves (128 query rows) per workgroup at d = 128
+    "w8d64": ["-DFA_WAVES_D64=8"],         # 8 waves (256 query rows) per workgroup at d = 64
+    "ahead1": ["-DFA_OPERAND_AHEAD=1"],    # MFMA operands requested one step pair ahead
+    "ahead3": ["-DFA_OPERAND_AHEAD=3"],    # three step pairs ahead
+}
 
 
-def build_library(verbose: bool = False) -> str:
-    out = lib_path()
+def lib_path(variant: str | None = None) -> str:
+    if variant is None:
+        return os.path.join(PKG, LIB_NAME)
+    return os.path.join(PKG, LIB_NAME.replace(".so", f"_{variant}.so"))
+
+
+def build_library(verbose: bool = False, variant: str | None = None) -> str:
+    out = lib_path(variant)
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+    extra = TILE_VARIANTS[variant] if variant is not None else []
+    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,4 +56,9 @@ def build_library(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build_library(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--tile-variant", choices=sorted(TILE_VARIANTS), default=None,
+                    help="build a tile candidate of the forward into its own library (measurement only)")
+    a = ap.parse_args()
+    print(build_library(verbose=True, variant=a.tile_variant))

@@ -77,10 +77,24 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 constexpr int kBC = 64;           // keys per K/V tile
+// Tile parameters are compile-time constants.  The defaults are the measured
+// choice; a build may override them to measure another candidate (the
+// library's own build does not).
+#ifndef FA_WAVES_D128
+#define FA_WAVES_D128 8
+#endif
+#ifndef FA_WAVES_D64
+#define FA_WAVES_D64 4
+#endif
+#ifndef FA_OPERAND_AHEAD
+#define FA_OPERAND_AHEAD 2
+#endif
 // Waves per workgroup (32 query rows each): 8 at d = 128 (one workgroup per
 // CU, 128 KiB of LDS), 4 at d = 64 (64 KiB, two workgroups per CU, whose
 // waves share the SIMDs and drift apart).
-template <int D> constexpr int kWavesOf = D == 64 ? 4 : 8;
+template <int D> constexpr int kWavesOf = D == 64 ? FA_WAVES_D64 : FA_WAVES_D128;
+static_assert(FA_WAVES_D128 == 4 || FA_WAVES_D128 == 8, "waves per workgroup at d = 128");
+static_assert(FA_WAVES_D64 == 4 || FA_WAVES_D64 == 8, "waves per workgroup at d = 64");
 template <int D> constexpr int kThreadsOf = kWavesOf<D> * 64;
 template <int D> constexpr int kBROf = kWavesOf<D> * 32;   // query rows per workgroup
 __host__ __device__ constexpr int rows_per_block(int d) { return d == 64 ? kBROf<64> : kBROf<128>; }
@@ -152,6 +166,16 @@ struct TileCopy {
 #endif
   }
 };
+
+// Wait until at most N of this wave's vector-memory operations are in
+// flight (copies complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else static_assert(N == 2 || N == 4 || N == 8, "copies per step");
+}
 
 // Combine a per-lane value with the lane 32 apart using the gfx950
 // cross-half swap (a VALU op; a shuffle would go through the LDS crossbar).
@@ -403,13 +427,11 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   constexpr int kPV = kKs * kCt;        // P V steps: (t, ct), ct fastest
   constexpr int kS = kDs * kKb;         // S steps: (ks, kb), kb fastest
   static_assert(kPV == kS, "P V and S step counts are interleaved one to one");
-  constexpr int kAhead = 2;             // step pairs whose operands are requested ahead
+  constexpr int kAhead = FA_OPERAND_AHEAD;   // step pairs whose operands are requested ahead
 
   // this wave's copies of K_{j+1}, V_{j-1} (issued two steps ago; the
   // previous step's copies may still be in flight) ...
-  if constexpr (G::kLoads == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  static_assert(G::kLoads == 1 || G::kLoads == 2, "copy count per step");
+  wait_vmcnt<2 * G::kLoads>();
   __builtin_amdgcn_s_barrier();                      // ... and everyone's; j-1's reads done
   __builtin_amdgcn_sched_barrier(0);
 
@@ -431,6 +453,7 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   // cover.
   constexpr int kCopies = 2 * G::kLoads;
   constexpr int kCopyEvery = kPV / kCopies;
+  static_assert(kCopyEvery >= 2 && kCopyEvery * kCopies == kPV, "copies spread over the step's MFMA pairs");
   auto copy = [&](int q) {
     if (q < G::kLoads) c.kcopy.issue(c.Kh, (j + 3) * kBC, c.kv_end, k_fill, c.wave, q);
     else c.vcopy.issue(c.Vh, (j + 1) * kBC, c.kv_end, v_fill, c.wave, q - G::kLoads);
@@ -632,8 +655,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
   for (int t = 0; t < kBC / 16; ++t) pa[t] = bf16x8{};
 
-  if constexpr (G::kLoads == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");   // K_0, K_1
-  else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  wait_vmcnt<2 * G::kLoads>();                          // K_0, K_1
   __syncthreads();
   scores<D>(lds + G::k_buf(0), c.k_off, qf, sa);       // S_{j0}
 
@@ -688,6 +710,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // spread over the banks.
   {
     constexpr int kChunks = G::kChunks;
+    static_assert(kWavesOf<D> * 32 * G::kRowBytes <= G::kRing * G::kTile, "staging fits the K ring");
     char* stage = lds + G::k_buf(0) + c.wave * 32 * G::kRowBytes;
     const float inv = qrow < N ? 1.0f / l_tot : 0.f;
 #pragma unroll

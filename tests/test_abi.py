@@ -207,3 +207,15 @@ def test_fp8_launch_shape_query(lib):
     with pytest.raises(fa.FaError):
         fa.fa_fwd_fp8_tile(1, 1, 16, 96, 0)
 
+
+
+def test_library_override_is_refused_once_loaded(lib):
+    with pytest.raises(RuntimeError):
+        fa.use_library("/nonexistent/libfa_mi355x_other.so")
+
+
+def test_tile_variant_libraries_are_named_apart():
+    from io_aware_exact_13_amd import build
+    names = {build.lib_path()} | {build.lib_path(v) for v in build.TILE_VARIANTS}
+    assert len(names) == 1 + len(build.TILE_VARIANTS)
+    assert all(flag.startswith("-DFA_") for fl in build.TILE_VARIANTS.values() for flag in fl)

@@ -53,22 +53,14 @@ ALL_WARM_S = 0.3
 
 KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "fwd_fp8": "fa_fp8.hip"}
 
-# HBM traffic per launch from two rocprofv3 --pmc runs of this script
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same
-# counter reads for a plain 512 MiB device copy (FETCH_SIZE reads half of the
-# bytes the copy moves, WRITE_SIZE all of them).  Keyed by workload and pass;
-# each entry records the sha256 of the kernel source the counters were taken
-# on (or of a later source shown to compile to the same kernel code), and is
-# reported only while that source is unchanged.
-FETCH_SCALE = 2.0
-WRITE_SCALE = 1.0
-MEASURED_TRAFFIC = {
-    # (workload, pass): (kernel source sha256, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("causal_b1h32_n16384_d128", "fwd"): (
-        "d03e47be951252f44ac3469b435e7c4f3635315c124d38ed61cab95baa1af45b", 3.35861e5, 1.33120e5),
-    ("causal_b1h32_n16384_d128", "fwd_fp8"): (
-        "deb0c661177148065729940e4d3f5a9e647df350effa3e6c234ee8590f294520", 1.54121e5, 1.33120e5),
-}
+# HBM traffic per launch comes from rocprofv3 counter runs summarised under
+# profiles/ (io_aware_exact_13_amd.profsum traffic): FETCH_SIZE and
+# WRITE_SIZE of the kernel, each scaled by what the counter reads for a plain
+# device copy of known size.  Each summary ends in a `traffic-record:` line
+# naming the workload, the pass and the sha256 of the kernel source the
+# counters were taken on; the figure is reported only while that source is
+# unchanged (otherwise traffic is null).
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_sha256(pass_="fwd"):
@@ -78,11 +70,53 @@ def kernel_source_sha256(pass_="fwd"):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def traffic_records():
+    """Every `traffic-record:` line under profiles/ as (file name, fields)."""
+    import glob
+    out = []
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.txt"))):
+        with open(path, encoding="utf-8") as f:
+            for ln in f:
+                if ln.startswith("traffic-record:"):
+                    fields = dict(kv.split("=", 1) for kv in ln.split(":", 1)[1].split())
+                    out.append((os.path.basename(path), fields))
+    return out
+
+
 def measured_traffic(name, pass_="fwd"):
-    entry = MEASURED_TRAFFIC.get((name, pass_))
-    if entry is None or entry[0] != kernel_source_sha256(pass_):
-        return None
-    return round(entry[1] * 1024 * FETCH_SCALE + entry[2] * 1024 * WRITE_SCALE)
+    """(bytes per launch, source description) from the newest matching record
+    taken on the current kernel source, or (None, reason)."""
+    sha = kernel_source_sha256(pass_)
+    stale = None
+    for fname, f in reversed(traffic_records()):
+        if f.get("workload") != name or f.get("pass") != pass_:
+            continue
+        if f.get("source_sha256") != sha:
+            stale = fname
+            continue
+        total = float(f["read_bytes"]) + float(f["write_bytes"])
+        return round(total), f"profiles/{fname} (counters on source sha256 {sha[:16]})"
+    return None, (f"not measured on this source (profiles/{stale} holds an older one)" if stale
+                  else "not measured")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def usable_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count()
 
 
 def log(msg):
@@ -126,7 +160,8 @@ def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, 
                   input_bits="normal"):
     """Time `steps` calls of the forward (or, with backward, of fa_bwd on the
     forward's outputs) with HIP events on the launch stream: returns the total
-    of the timed region and the sorted per-call durations, in ms.  After the
+    of the timed region, the sorted per-call durations, in ms, and the
+    SHA-256 of the bf16 inputs' bytes (q, k, v).  After the
     `warmup` calls, untimed calls continue until `warm_s` seconds have passed
     (0: none), so that the shader clock has left its idle level before a
     short workload is timed."""
@@ -135,7 +170,10 @@ def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, 
     import workloads
 
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in diagnostic_inputs(workloads.make_inputs(w), input_bits))
+    host = diagnostic_inputs(workloads.make_inputs(w), input_bits)
+    shas = {name: workloads.sha256_of(t) for name, t in zip("qkv", host)}
+    q, k, v = (t.to(dev) for t in host)
+    del host
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -196,7 +234,7 @@ def time_workload(w, steps, warmup, backward=False, n_splits=0, fa1order=False, 
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    return total_ms, per
+    return total_ms, per, shas
 
 
 def time_quant_fp8(w, steps, warmup):
@@ -249,6 +287,7 @@ def cpu_baseline_fp8(w):
     dt = time.perf_counter() - t0
     flops = 4.0 * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "cpu_model": cpu_model(), "usable_cores": usable_cores(), "blas_threads": int(blas_threads()),
             "sample": f"1 of {w.B * w.H} heads of {w.name} (all {w.N} query rows), FP8 oracle "
                       f"(quantisation + online softmax with E4M3 P, fp64 numpy), {dt:.1f} s"}
 
@@ -274,8 +313,48 @@ def cpu_baseline(w, n_heads=32, backward=False):
     dt = time.perf_counter() - t0
     flops = 4.0 * w.N * w.N * w.d * n_heads / (2.0 if w.causal else 1.0) * (2.5 if backward else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "usable_cores": usable_cores(), "blas_threads": int(threads),
             "sample": f"{n_heads} of {w.B * w.H} heads of {w.name} (all {w.N} query rows each), "
                       f"{'gradients, ' if backward else ''}fp64 numpy, {dt:.1f} s"}
+
+
+def gemm_calibration(m, steps, warmup, warm_s):
+    """Time torch.matmul on bf16 [m, m] x [m, m] N(0,1) inputs (contiguous, no
+    transposed view) on the launch stream and print one JSON line: the rate a
+    library GEMM reaches on this GPU under the same power limit, a measured
+    ceiling beside the published peak."""
+    import torch
+    from io_aware_exact_13_amd import accounting as acc
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(11)
+    a = torch.randn((m, m), generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+    b = torch.randn((m, m), generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+    c = torch.empty((m, m), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record(stream)
+        torch.matmul(a, b, out=c)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
+    mean = sum(per) / len(per)
+    flops = 2.0 * m ** 3
+    tf = flops / (mean * 1e-3) / 1e12
+    log(f"[bench] bf16 GEMM {m}^3: mean {mean:.4f} ms, median {per[len(per) // 2]:.4f} ms -> {tf:.1f} TFLOP/s "
+        f"({100 * tf / acc.PEAK_BF16_DENSE_TFLOPS:.1f}% of the bf16 dense peak)")
+    print(json.dumps({"metric": "bf16 GEMM TFLOP/s (torch.matmul, N(0,1) inputs)", "value": round(tf, 2),
+                      "unit": "TFLOP/s", "M": m, "steps": steps, "warmup": warmup,
+                      "launch_ms": {"mean": round(mean, 5), "median": round(per[len(per) // 2], 5),
+                                    "min": round(per[0], 5)},
+                      "frac_of_peak": round(tf / acc.PEAK_BF16_DENSE_TFLOPS, 4)}), flush=True)
 
 
 def main():
@@ -301,6 +380,9 @@ def main():
     ap.add_argument("--fp8", action="store_true", help="measure the FP8 forward fa_fwd_fp8 instead of fa_fwd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 3 times (counter calibration)")
+    ap.add_argument("--gemm-calibration", type=int, default=0, metavar="M",
+                    help="only time a plain bf16 M x M x M matrix product (torch.matmul, the vendor GEMM "
+                         "library) on N(0,1) inputs: the MFMA rate this GPU sustains on a dense contraction")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: only --gpus 1 is supported: the kernel and its measurement cover one GPU", file=sys.stderr)
@@ -325,6 +407,9 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copied 512 MiB three times")
         return
+    if args.gemm_calibration:
+        gemm_calibration(args.gemm_calibration, args.steps, args.warmup, args.warm_s)
+        return
 
     if args.shape:
         B, H, N, d, causal = (int(x) for x in args.shape.split(","))
@@ -339,7 +424,7 @@ def main():
     log_sclk("before")
     if args.splitkv < 0:
         args.splitkv = fa.fa_fwd_splitkv_plan(w.B, w.H, w.N, w.d, int(w.causal))[0]
-    total_ms, per = time_workload(w, args.steps, args.warmup, backward=args.bwd,
+    total_ms, per, shas = time_workload(w, args.steps, args.warmup, backward=args.bwd,
                                   n_splits=0 if args.bwd else args.splitkv, fa1order=args.fa1order, fp8=args.fp8,
                                   warm_s=args.warm_s, input_bits=args.input_bits)
     log_sclk("after")
@@ -366,7 +451,7 @@ def main():
             other = ow.name
             for mode in ("fwd", "bwd", "fp8"):
                 bw = mode == "bwd"
-                tms, p = time_workload(ow, ALL_STEPS, 3, backward=bw, fp8=mode == "fp8", warm_s=ALL_WARM_S)
+                tms, p, _ = time_workload(ow, ALL_STEPS, 3, backward=bw, fp8=mode == "fp8", warm_s=ALL_WARM_S)
                 f = (acc.attention_bwd_flops if bw else acc.attention_flops)(ow.B, ow.H, ow.N, ow.d, ow.causal)
                 t = tms / ALL_STEPS
                 pk = acc.PEAK_FP8_DENSE_TFLOPS if mode == "fp8" else acc.PEAK_BF16_DENSE_TFLOPS
@@ -379,13 +464,15 @@ def main():
             plan = fa.fa_fwd_splitkv_plan(sw.B, sw.H, sw.N, sw.d, int(sw.causal))[0]
             f = acc.attention_flops(sw.B, sw.H, sw.N, sw.d, sw.causal)
             for ns in sorted({0, 2, plan, 8}):
-                tms, p = time_workload(sw, ALL_STEPS, 3, n_splits=ns, warm_s=ALL_WARM_S)
+                tms, p, _ = time_workload(sw, ALL_STEPS, 3, n_splits=ns, warm_s=ALL_WARM_S)
                 t = tms / ALL_STEPS
                 log(f"[bench-all] {sw.name:32s} {'fwd' if ns == 0 else f'split{ns}':>7s} {t * 1e3:9.1f} us  "
                     f"{f / (t * 1e-3) / 1e12:7.1f} TFLOP/s{'  (plan)' if ns == plan else ''}")
 
-    traffic = (None if (args.bwd or args.splitkv or args.fa1order or args.lib) else
-               measured_traffic(name, "fwd_fp8" if args.fp8 else "fwd"))
+    if args.bwd or args.splitkv or args.fa1order or args.lib:
+        traffic, traffic_source = None, "not measured for this pass or library"
+    else:
+        traffic, traffic_source = measured_traffic(name, "fwd_fp8" if args.fp8 else "fwd")
     result = {
         "metric": METRIC_BWD if args.bwd else (METRIC_FP8 if args.fp8 else METRIC),
         "value": round(value, 2),
@@ -404,6 +491,7 @@ def main():
                    "pass": "bwd" if args.bwd else ("fwd_fa1order" if args.fa1order else "fwd_fp8" if args.fp8 else
                                                    (f"fwd_splitkv{args.splitkv}" if args.splitkv else "fwd")), "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "seed": w.seed,
+                   "inputs_sha256": shas,
                    **({"untimed_warm_s": args.warm_s} if args.warm_s else {}),
                    **({"library": os.path.basename(args.lib)} if args.lib else {}),
                    "pct_of_bf16_peak": round(100 * value / acc.PEAK_BF16_DENSE_TFLOPS, 2),
@@ -416,7 +504,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "traffic_source": traffic_source},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")

@@ -1,18 +1,28 @@
-"""Compile the HIP library for gfx950 in-tree (hipcc cross-compiles without a GPU)."""
+"""Compile the HIP library for gfx950 in-tree (hipcc cross-compiles without a GPU).
+
+Each source is compiled to its own object (with its own embedded gfx950 code
+object), in parallel, and the objects are linked into one shared library.
+Build variants override compile-time constants of the forward source only and
+reuse the other objects.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 LIB_NAME = "libfa_mi355x.so"
-SOURCES = [os.path.join(PKG, "csrc", name) for name in ("fa_fwd.hip", "fa_bwd.hip", "fa_fa1.hip", "fa_fp8.hip", "fa_quant8.hip")]
+OBJ_DIR = os.path.join(PKG, "_build")
+FWD_SOURCE = "fa_fwd.hip"
+SOURCE_NAMES = (FWD_SOURCE, "fa_bwd.hip", "fa_fa1.hip", "fa_fp8.hip", "fa_quant8.hip")
+SOURCES = [os.path.join(PKG, "csrc", name) for name in SOURCE_NAMES]
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-I" + os.path.join(ROOT, "include"),
     # no packed-fp32 VALU instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -20,14 +30,19 @@ FLAGS = [
 ]
 
 
-# Tile candidates of the bf16 forward, for measurement only: each overrides
-# compile-time constants of fa_fwd.hip (the default build overrides none).
+# Variants of the bf16 forward, each overriding compile-time constants of
+# fa_fwd.hip (the default build overrides none).  The tile candidates are for
+# measurement only; "exactmax" and "racecheck" are also built by the default
+# build, because GPU tests compare them with the default library.
 TILE_VARIANTS = {
     "w4d128": ["-DFA_WAVES_D128=4"],       # 4 waves (128 query rows) per workgroup at d = 128
     "w8d64": ["-DFA_WAVES_D64=8"],         # 8 waves (256 query rows) per workgroup at d = 64
     "ahead1": ["-DFA_OPERAND_AHEAD=1"],    # MFMA operands requested one step pair ahead
     "ahead3": ["-DFA_OPERAND_AHEAD=3"],    # three step pairs ahead
+    "exactmax": ["-DFA_EXACT_MAX=1"],      # reference maximum = running row maximum (no lag)
+    "racecheck": ["-DFA_EXTRA_BARRIER=1"],  # a wait and a workgroup barrier after every step's LDS reads
 }
+TEST_VARIANTS = ("exactmax", "racecheck")
 
 
 def lib_path(variant: str | None = None) -> str:
@@ -36,11 +51,7 @@ def lib_path(variant: str | None = None) -> str:
     return os.path.join(PKG, LIB_NAME.replace(".so", f"_{variant}.so"))
 
 
-def build_library(verbose: bool = False, variant: str | None = None) -> str:
-    out = lib_path(variant)
-    tmp = out + ".tmp"
-    extra = TILE_VARIANTS[variant] if variant is not None else []
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,14 +62,62 @@ def build_library(verbose: bool = False, variant: str | None = None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
+
+
+def _obj(name: str, variant: str | None) -> str:
+    stem = name.replace(".hip", "")
+    return os.path.join(OBJ_DIR, f"{stem}{'_' + variant if variant else ''}.o")
+
+
+def _compile(src: str, obj: str, extra, verbose):
+    tmp = obj + ".tmp"
+    _run([HIPCC, *FLAGS, *extra, "-c", src, "-o", tmp], verbose)
+    os.replace(tmp, obj)
+
+
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
-    return out
+
+
+def build_all(verbose: bool = False, variants=()) -> list[str]:
+    """Compile every source (and the forward once per variant) in parallel,
+    then link the default library and one library per variant."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    jobs = [(src, _obj(name, None), []) for name, src in zip(SOURCE_NAMES, SOURCES)]
+    fwd_src = SOURCES[SOURCE_NAMES.index(FWD_SOURCE)]
+    jobs += [(fwd_src, _obj(FWD_SOURCE, v), TILE_VARIANTS[v]) for v in variants]
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(_compile, s, o, e, verbose) for s, o, e in jobs]:
+            f.result()
+    common = [_obj(n, None) for n in SOURCE_NAMES if n != FWD_SOURCE]
+    outs = [lib_path()]
+    _link([_obj(FWD_SOURCE, None), *common], outs[0], verbose)
+    for v in variants:
+        outs.append(lib_path(v))
+        _link([_obj(FWD_SOURCE, v), *common], outs[-1], verbose)
+    return outs
+
+
+def build_library(verbose: bool = False, variant: str | None = None) -> str:
+    """Build the default library, or the default plus one variant's library;
+    returns the path of the one asked for."""
+    outs = build_all(verbose, () if variant is None else (variant,))
+    return outs[-1]
 
 
 if __name__ == "__main__":
     import argparse
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--tile-variant", choices=sorted(TILE_VARIANTS), default=None,
-                    help="build a tile candidate of the forward into its own library (measurement only)")
+                    help="also build a variant of the forward into its own library")
+    ap.add_argument("--all-variants", action="store_true", help="build every variant")
     a = ap.parse_args()
-    print(build_library(verbose=True, variant=a.tile_variant))
+    if a.all_variants:
+        print("\n".join(build_all(verbose=True, variants=tuple(TILE_VARIANTS))))
+    elif a.tile_variant:
+        print(build_library(verbose=True, variant=a.tile_variant))
+    else:
+        print("\n".join(build_all(verbose=True, variants=TEST_VARIANTS)))

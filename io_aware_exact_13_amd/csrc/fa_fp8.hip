@@ -235,7 +235,9 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[2], int key0, int lim,
   const bool grow = m_tile > st.m_ref;
   const float m_new = grow ? m_tile : st.m_ref;
   *rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
-  const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first tile
+  // 0 while the row has seen no key (acc and l are still 0): no exp2 of
+  // (-inf) - (-inf) when this tile shows it none either
+  const float alpha = (st.m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
   st.m_ref = m_new;
   const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
   float l4[4] = {0.f, 0.f, 0.f, 0.f};

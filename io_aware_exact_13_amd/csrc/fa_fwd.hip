@@ -103,8 +103,23 @@ constexpr int kXcds = 8;          // accelerator dies; workgroups are dealt to t
 constexpr int kMaxSplits = 64;    // key ranges per query block in the split-KV forward
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Reference maximum.  By default it lags the running row maximum (see
+// softmax_tile and softmax_tile_lagged).  A build with FA_EXACT_MAX=1 keeps
+// the reference at the running maximum itself, so the largest weight seen so
+// far is exactly 1 (for measuring what the lag costs in accuracy and saves in
+// time).
+#ifndef FA_EXACT_MAX
+#define FA_EXACT_MAX 0
+#endif
+// A build with FA_EXTRA_BARRIER=1 adds, after every step's LDS reads, a wait
+// for all of the wave's memory operations and a workgroup barrier: slower,
+// and its results must equal the default build's bit for bit (a race on the
+// LDS rings would show as a difference).
+#ifndef FA_EXTRA_BARRIER
+#define FA_EXTRA_BARRIER 0
+#endif
 constexpr float kPMax = 4294967296.0f;   // 2^32: largest tile sum of P a lane may reach before the reference moves
-constexpr float kSlack = 8.0f;    // log2 units the reference max may lag the true max
+constexpr float kSlack = FA_EXACT_MAX ? 0.0f : 8.0f;    // log2 units the reference max may lag the true max
 
 // LDS geometry: unpadded rows with XOR-swizzled 16-byte chunks, so a tile is
 // exactly 16 KiB (d=128) and every wave copies the same number of 1 KiB
@@ -278,7 +293,9 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, i
   const bool grow = m_tile > st.m_ref + kSlack;
   const float m_new = grow ? m_tile : st.m_ref;
   *rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
-  const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);   // 0 on the first tile
+  // 0 while the row has seen no key (acc and l are still 0): no exp2 of
+  // (-inf) - (-inf) when this tile shows it none either
+  const float alpha = (st.m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
   st.m_ref = m_new;
   const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
   // P is summed in fp32 (the logsumexp needs the unrounded weights) and
@@ -468,7 +485,7 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   }
   // d = 64: the lagged reference without a row maximum (about 5% faster
   // there; no gain for d = 128, whose MFMA work per tile hides the max tree)
-  constexpr bool kNoMax = (D == 64);
+  constexpr bool kNoMax = (D == 64) && !FA_EXACT_MAX;
   bool rescale = false;
   float alpha = 1.f, lt = 0.f;
   if constexpr (kNoMax) rescale = softmax_tile_lagged<MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st.m_ref, p_out, &lt);
@@ -485,6 +502,12 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i % kCopyEvery == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+  }
+  if constexpr (FA_EXTRA_BARRIER) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (kNoMax) {
     if (rescale) {

@@ -64,6 +64,77 @@ def compare_full(q, k, v, scale, causal, o, lse, with_rounding=False, p_rounding
     return do.max(), do.mean(), dl.max()
 
 
+def compare_all_heads(q, k, v, scale, causal, o, lse, workers=None):
+    """Every element of every (b, h) against the oracle, one head per task on
+    a thread pool (the oracle's BLAS calls and ufuncs release the GIL).
+    q, k, v: CPU bf16 [B, H, N, d]; o (bf16), lse (fp32): the GPU results on
+    the CPU.  Returns max|dO|, mean|dO| over the whole tensor, max|dLSE| and
+    max(|dO| - half a bf16 ulp of the oracle's O)."""
+    from concurrent.futures import ThreadPoolExecutor
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    B, H = q.shape[:2]
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cores = min(cores, 16)
+    workers = workers or max(1, min(8, cores // 2, B * H))
+
+    def head(bh):
+        b, h = divmod(bh, H)
+        ro, rl = oracle.attention_head_rows(q[b, h].double().numpy(), k[b, h].double().numpy(),
+                                            v[b, h].double().numpy(), scale, causal)
+        d = np.abs(o[b, h].double().numpy() - ro)
+        dl = np.abs(lse[b, h].double().numpy() - rl)
+        return float(d.max()), float(d.sum()), d.size, float(dl.max()), float((d - bf16_half_ulp(ro)).max())
+
+    def run():
+        with ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(head, range(B * H)))
+
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=max(1, cores // workers)):
+            res = run()
+    else:
+        res = run()
+    mo = max(r[0] for r in res)
+    me = sum(r[1] for r in res) / sum(r[2] for r in res)
+    ml = max(r[3] for r in res)
+    beyond = max(r[4] for r in res)
+    return mo, me, ml, beyond
+
+
+_variant_libs = {}
+
+
+def variant_fwd(variant, q, k, v, scale, causal):
+    """fa_fwd of a variant build of the library (build.py TEST_VARIANTS),
+    loaded beside the default one through its own handle; q, k, v on the GPU.
+    Returns (o, lse) after a synchronisation."""
+    import ctypes
+    from io_aware_exact_13_amd.build import lib_path
+    lib = _variant_libs.get(variant)
+    if lib is None:
+        path = lib_path(variant)
+        if not os.path.exists(path):
+            raise RuntimeError(f"variant library {path} is not built")
+        lib = ctypes.CDLL(path)
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+        lib.fa_fwd.restype = ci
+        _variant_libs[variant] = lib
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device)
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                    ctypes.c_float(scale), int(bool(causal)), stream.cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"{variant} fa_fwd returned {st}")
+    torch.cuda.synchronize()
+    return o, lse
+
+
 def compare_rows(q, k, v, scale, causal, o, lse, picks):
     """picks: list of (b, h, rows).  Returns max|dO|, mean|dO|, max|dLSE| over them."""
     worst_o, worst_l, tot, cnt = 0.0, 0.0, 0.0, 0

@@ -31,12 +31,24 @@ def test_const_inputs_are_one_half_everywhere():
     assert all(bool((t == 0.5).all()) and t.dtype == torch.bfloat16 for t in out)
 
 
-def test_traffic_is_reported_only_for_the_source_it_was_measured_on(monkeypatch):
-    name, pass_ = next(iter(bench.MEASURED_TRAFFIC))
-    sha, fetch_kib, write_kib = bench.MEASURED_TRAFFIC[(name, pass_)]
+def test_traffic_is_reported_only_for_the_source_it_was_measured_on(monkeypatch, tmp_path):
+    sha = "ab" * 32
+    (tmp_path / "k_counters.txt").write_text(
+        "summary text\n"
+        f"traffic-record: workload=w1 pass=fwd source=fa_fwd.hip source_sha256={sha} "
+        "read_bytes=6.0e8 write_bytes=1.5e8\n")
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_sha256", lambda p="fwd": sha)
-    assert bench.measured_traffic(name, pass_) == round(
-        fetch_kib * 1024 * bench.FETCH_SCALE + write_kib * 1024 * bench.WRITE_SCALE)
+    traffic, src = bench.measured_traffic("w1", "fwd")
+    assert traffic == 750000000 and "k_counters.txt" in src and sha[:16] in src
     monkeypatch.setattr(bench, "kernel_source_sha256", lambda p="fwd": "0" * 64)
-    assert bench.measured_traffic(name, pass_) is None
-    assert bench.measured_traffic("no_such_workload", pass_) is None
+    traffic, src = bench.measured_traffic("w1", "fwd")
+    assert traffic is None and "older" in src
+    assert bench.measured_traffic("no_such_workload", "fwd")[0] is None
+    assert bench.measured_traffic("w1", "fwd_fp8")[0] is None
+
+
+def test_committed_traffic_records_parse():
+    for fname, fields in bench.traffic_records():
+        assert {"workload", "pass", "source_sha256", "read_bytes", "write_bytes"} <= set(fields), fname
+        assert float(fields["read_bytes"]) > 0 and float(fields["write_bytes"]) > 0

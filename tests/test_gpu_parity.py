@@ -1,5 +1,8 @@
 """The HIP path against the fp64 oracle, element by element (GPU only)."""
+import json
 import math
+import os
+import time
 
 import numpy as np
 import pytest
@@ -7,10 +10,19 @@ import torch
 
 import io_aware_exact_13_amd as fa
 import workloads
-from gpu_common import (O_MAX_ABS, O_MEAN_ABS, LSE_MAX_ABS, announce, compare_full, compare_rows,
-                        device, run_gpu, sample_picks, to64)
+from gpu_common import (O_MAX_ABS, O_MEAN_ABS, LSE_MAX_ABS, announce, compare_all_heads, compare_full,
+                        compare_rows, device, run_gpu, sample_picks, to64, variant_fwd)
 
 pytestmark = pytest.mark.gpu
+
+
+def log_parity(name, mo, me, ml, beyond):
+    """Append one workload's figures to the JSON-lines file FA_PARITY_LOG names (if set)."""
+    path = os.environ.get("FA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"workload": name, "max_abs_dO": mo, "mean_abs_dO": me, "max_abs_dLSE": ml,
+                                "max_dO_beyond_bf16_rounding": beyond}) + "\n")
 
 # Small shapes the oracle finishes in seconds: several query blocks (128 rows)
 # and key tiles (64 keys), ragged tails, both head dims, with and without mask.
@@ -72,9 +84,10 @@ def test_tiny_workload_full_compare():
 
 
 @pytest.mark.parametrize("name", [n for n in workloads.WORKLOAD_ORDER if n != "tiny_b1h1_n256_d64"])
-def test_full_size_workloads_on_sampled_rows(name):
-    """Full sizes, the launch the benchmark times; the oracle recomputes sampled
-    rows one head at a time; finiteness and the convex-hull bound hold everywhere."""
+def test_full_size_workloads_every_element(name):
+    """Full sizes, in the launch the benchmark times: every element of O and
+    LSE of every head against the oracle, held to the bar outright (mean over
+    the whole tensor); the output is also bitwise equal run to run."""
     w = workloads.WORKLOADS[name]
     announce(f"[parity-full] {name}: generating inputs")
     q, k, v = workloads.make_inputs(w)
@@ -88,13 +101,13 @@ def test_full_size_workloads_on_sampled_rows(name):
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), l2.view(torch.int32))
     del qd, kd, vd, o2, l2
-    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
-    vmax = v.float().abs().amax().item()
-    assert o.float().abs().amax().item() <= vmax * (1 + 2 ** -8)
-    picks = sample_picks(w, n_heads=4 if w.B * w.H > 4 else 2, seed=w.seed)
-    mo, me, ml = compare_rows(q, k, v, w.scale, w.causal, o, lse, picks)
-    announce(f"    rows={sum(len(r) for _, _, r in picks)} max|dO|={mo:.3e} mean|dO|={me:.3e} "
-             f"max|dLSE|={ml:.3e}")
+    o, lse = o.cpu(), lse.cpu()
+    announce(f"[parity-full] {name}: oracle over all {w.B * w.H} heads")
+    t0 = time.perf_counter()
+    mo, me, ml, beyond = compare_all_heads(q, k, v, w.scale, w.causal, o, lse)
+    announce(f"[parity-full] {name}: max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e} "
+             f"(max|dO| beyond O's bf16 rounding {beyond:.3e}; oracle {time.perf_counter() - t0:.1f} s)")
+    log_parity(name, mo, me, ml, beyond)
     assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
 
 
@@ -259,3 +272,53 @@ def test_caller_buffers_of_the_wrong_shape_dtype_or_layout_are_rejected():
         fa.fwd(q, k.cpu(), v, causal=True)
     torch.cuda.synchronize()
     assert (short_o == 3.0).all().item() and (short_l == 3.0).all().item()
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,workload", [
+    (2, 4, 777, 128, True, None), (1, 3, 333, 64, False, None), (1, 2, 1000, 64, True, None),
+    (3, 1, 1025, 128, True, None), (0, 0, 0, 0, False, "mid_b4h16_n4096_d128")])
+def test_extra_barrier_build_is_bitwise_equal(B, H, N, d, causal, workload):
+    """The race-check build waits for every memory operation and holds a
+    workgroup barrier after each step's LDS reads, so no wave can refill an
+    LDS ring buffer another wave may still read.  Its results must equal the
+    default build's bit for bit: a race on the rings (the on-chip tiles the
+    tiled method reuses across the key loop) would show as a difference."""
+    dev = device()
+    w = workloads.WORKLOADS[workload] if workload else workloads.custom(B, H, N, d, causal, seed=31 + N)
+    announce(f"[racecheck] {w.name}")
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
+    o2, l2 = variant_fwd("racecheck", q, k, v, w.scale, w.causal)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), l2.view(torch.int32))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_exact_running_max_build_keeps_a_late_dominant_key_exact(d):
+    """The build whose reference maximum is the running row maximum itself
+    (the online softmax as the pages write it: m_new = max(m, rowmax S)):
+    the dominant key's weight is exp(0) = 1, exact in bf16, so on the
+    late-dominant-key rows O is held to 1e-2 beyond its own output rounding
+    alone, and LSE and mean|dO| outright."""
+    dev = device()
+    w = workloads.custom(1, 2, 900, d, True, seed=600 + d)
+    q, k, v = workloads.make_inputs(w)
+    k[:, :, 700] = (q[:, :, 750].float() * 8).to(torch.bfloat16)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    for scale in (w.scale, 0.5):
+        o, lse = variant_fwd("exactmax", qd, kd, vd, scale, True)
+        beyond, me, ml, raw = compare_full(q, k, v, scale, True, o, lse, with_rounding=True)
+        announce(f"[exact max, late key d={d} scale {scale:.3f}] max|dO|={raw:.3e} "
+                 f"(beyond O's rounding {beyond:.3e}) mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+        assert beyond <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 3, 700, 128, True), (2, 2, 513, 64, False), (1, 2, 1000, 64, True)])
+def test_exact_running_max_build_matches_oracle(B, H, N, d, causal):
+    dev = device()
+    w = workloads.custom(B, H, N, d, causal, seed=1000 + N + d + int(causal))
+    q, k, v = workloads.make_inputs(w)
+    o, lse = variant_fwd("exactmax", q.to(dev), k.to(dev), v.to(dev), w.scale, causal)
+    mo, me, ml = compare_full(q, k, v, w.scale, causal, o, lse)
+    announce(f"[exact max] {w.name}: max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS

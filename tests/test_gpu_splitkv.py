@@ -1,5 +1,7 @@
 """The split-KV forward (fa_fwd_splitkv) against the fp64 oracle, with the
 forward's bar: it computes the same function as fa_fwd (GPU only)."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -75,3 +77,40 @@ def test_splitkv_is_bitwise_deterministic():
     b = run_split(q, k, v, w.scale, True, 3)
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,n_splits", [(1, 2, 300, 128, True, 5), (1, 2, 300, 64, True, 5),
+                                                     (2, 1, 700, 64, True, 7), (1, 1, 130, 128, False, 4)])
+def test_partials_of_rows_without_a_visible_key_are_exact_zeros(B, H, N, d, causal, n_splits):
+    """Ranges that start past some rows of a query block leave those rows no
+    visible key: their partials must be exactly O_s = 0 and LSE_s = -inf (they
+    drop out of the two-block merge of the online softmax), and no partial
+    anywhere may hold a NaN (the running statistics of such a row start at
+    -inf and must not form (-inf) - (-inf))."""
+    dev = device()
+    w = workloads.custom(B, H, N, d, causal, seed=4000 + N + d)
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    o_part = torch.full((n_splits, B, H, N, d), 7.0, dtype=torch.float32, device=dev)
+    lse_part = torch.full((n_splits, B, H, N), 7.0, dtype=torch.float32, device=dev)
+    o, lse = fa.fwd_splitkv(q, k, v, scale=w.scale, causal=causal, n_splits=n_splits, o_part=o_part,
+                            lse_part=lse_part)
+    torch.cuda.synchronize()
+    op, lp = o_part.cpu(), lse_part.cpu()
+    assert not torch.isnan(op).any().item() and not torch.isnan(lp).any().item()
+    br, kc = fa.fa_fwd_tile(B, H, N, d, int(causal))[:2]
+    n_empty = 0
+    for i in range(N):
+        q0 = (i // br) * br
+        tiles = -(-(min(N, q0 + br) if causal else N) // kc)
+        for s in range(n_splits):
+            j0, j1 = s * tiles // n_splits, (s + 1) * tiles // n_splits
+            visible = j0 < j1 and (not causal or j0 * kc <= i)
+            if visible:
+                assert torch.isfinite(op[s, :, :, i]).all().item() and torch.isfinite(lp[s, :, :, i]).all().item()
+            else:
+                n_empty += 1
+                assert (op[s, :, :, i] == 0).all().item() and (lp[s, :, :, i] == -math.inf).all().item()
+    announce(f"[splitkv-empty] {w.name} n_splits={n_splits}: {n_empty} (row, range) pairs with no visible key")
+    assert n_empty > 0
+    mo, me, ml = compare_full(*(t.cpu() for t in (q, k, v)), w.scale, causal, o, lse)
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS

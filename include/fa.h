@@ -43,6 +43,11 @@ extern "C" {
 #define FA_ERR_FLAG      -7  /* causal is not 0 or 1                                        */
 #define FA_ERR_ALIAS     -8  /* an output buffer overlaps an input or another output        */
 #define FA_ERR_SPLITS    -9  /* n_splits is not between 1 and 64                            */
+#define FA_ERR_SCRATCH  -10  /* B*H*N exceeds the library's own workspace (FA_NOALLOC_ROWS) */
+#define FA_ERR_DEVICE   -11  /* the current device or the workspace's address is unavailable */
+
+/* Rows (B*H*N) that fa_bwd_noalloc's own workspace holds: 2^21 fp32 values. */
+#define FA_NOALLOC_ROWS  (1 << 21)
 
 /*
  * fa_fwd -- enqueue the attention forward on `stream` and return.
@@ -178,6 +183,29 @@ int fa_fwd_fa1order(const void* q, const void* k, const void* v, void* o, float*
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, float* delta,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels and results (bitwise equal to fa_bwd's), with
+ * the D workspace taken from the library's own device array instead of a
+ * `delta` argument.
+ *
+ * Arguments: those of fa_bwd without delta.
+ * Limit: B*H*N <= FA_NOALLOC_ROWS (2^21 rows, 8 MiB of fp32 per GPU),
+ * otherwise FA_ERR_SCRATCH and nothing is launched.
+ * Device: the kernels run on `stream`, which must belong to the current
+ * device.  The first call on a device looks up that device's copy of the
+ * array (FA_ERR_DEVICE if that fails) and keeps its address; each GPU holds
+ * its copy until the process ends.  The call allocates nothing and calls no
+ * allocating routine.
+ * Concurrency: every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (other streams, other host threads) race; order
+ * them on one stream or use fa_bwd with a workspace per caller.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
  * FP8 forward.  Source: "为什么Flash Attention能将注意力计算提速数倍而不损失精度",

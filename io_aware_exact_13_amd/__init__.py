@@ -23,6 +23,9 @@ FA_ERR_LAUNCH = -6
 FA_ERR_FLAG = -7
 FA_ERR_ALIAS = -8
 FA_ERR_SPLITS = -9
+FA_ERR_SCRATCH = -10
+FA_ERR_DEVICE = -11
+NOALLOC_ROWS = 1 << 21     # rows (B*H*N) fa_bwd_noalloc's own workspace holds
 
 _lib = None
 
@@ -66,6 +69,8 @@ def load_library():
     lib.fa_fwd_tile.restype = ci
     lib.fa_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_bwd.restype = ci
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    lib.fa_bwd_noalloc.restype = ci
     lib.fa_fwd_splitkv.argtypes = [vp] * 5 + [ci, ci, ci, ci, ctypes.c_float, ci, ci, vp, vp, vp]
     lib.fa_fwd_splitkv.restype = ci
     lib.fa_fwd_splitkv_plan.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_size_t),
@@ -95,6 +100,12 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, 
     """C-ABI fa_bwd with raw device addresses (ints); returns the status code."""
     return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d,
                                  ctypes.c_float(scale), int(causal), stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream) -> int:
+    """C-ABI fa_bwd_noalloc with raw device addresses (ints); returns the status code."""
+    return load_library().fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d,
+                                         ctypes.c_float(scale), int(causal), stream)
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, n_splits, o_part, lse_part, stream) -> int:
@@ -243,6 +254,33 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
                 int(bool(causal)), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale=None, causal=False, stream=None):
+    """fa_bwd through the entry point that allocates nothing (its D workspace
+    is the library's own device array): the caller passes every output.
+    B*H*N must not exceed NOALLOC_ROWS; calls that overlap in time on one GPU
+    race on that array."""
+    import torch
+    ts = (q, k, v, o, dout)
+    if any(t.dtype != torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
+        raise TypeError("q, k, v, o, dout must be bfloat16 and lse float32")
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts) or lse.shape != q.shape[:3]:
+        raise ValueError("q, k, v, o, dout must share one [B, H, N, d] shape and lse be [B, H, N]")
+    _check_inputs(ts + (lse,), ("q", "k", "v", "o", "dout", "lse"), q.device)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_buffer(t, name, torch.bfloat16, q.shape, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                        stream.cuda_stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

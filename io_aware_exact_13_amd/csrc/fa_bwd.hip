@@ -34,8 +34,16 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "cdna4.h"
 #include "fa.h"
+
+// Device memory of fa_bwd_noalloc: its D workspace, FA_NOALLOC_ROWS fp32
+// values (8 MiB), one copy per GPU, held until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in): it
+// looks up each device's address once and passes that.
+static __device__ __align__(256) float scratch[FA_NOALLOC_ROWS];
 
 namespace {
 
@@ -359,10 +367,13 @@ void launch_bwd(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16*
 
 }  // namespace
 
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
-                      int d, float scale, int causal, hipStream_t stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+// Host checks shared by fa_bwd and fa_bwd_noalloc (delta == nullptr: the
+// workspace is the library's own).  Returns FA_OK or an FA_ERR_* code; no
+// HIP call.
+static int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, float* delta, bool own_delta, int B, int H,
+                     int N, int d, float scale, int causal) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || (!own_delta && !delta)) return FA_ERR_NULL;
   if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
@@ -372,6 +383,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   if (bh > 0x7fffffffLL || blocks * kThreads > 0xffffffffLL || rows > 0x7fffffffLL * 16LL ||
       (long long)N * d * 2 >= 0x80000000LL)
     return FA_ERR_SHAPE;
+  if (own_delta && rows > FA_NOALLOC_ROWS) return FA_ERR_SCRATCH;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
@@ -384,14 +396,20 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   const size_t in_bytes[6] = {tb, tb, tb, tb, lb, tb};
   void* outs[4] = {dq, dk, dv, delta};
   const size_t out_bytes[4] = {tb, tb, tb, lb};
-  for (int a = 0; a < 4; ++a) {
+  const int n_outs = own_delta ? 3 : 4;
+  for (int a = 0; a < n_outs; ++a) {
     for (int b = 0; b < 6; ++b)
       if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_ALIAS;
-    for (int b = a + 1; b < 4; ++b)
+    for (int b = a + 1; b < n_outs; ++b)
       if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
   }
+  return FA_OK;
+}
 
-  const int BHi = (int)bh;
+static void dispatch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                         int d, float scale, int causal, hipStream_t stream) {
+  const int BHi = B * H;
   const __bf16* Q = static_cast<const __bf16*>(q);
   const __bf16* Kp = static_cast<const __bf16*>(k);
   const __bf16* Vp = static_cast<const __bf16*>(v);
@@ -407,5 +425,53 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     if (causal) launch_bwd<64, true>(Q, Kp, Vp, Op, lse, dOp, dQp, dKp, dVp, delta, BHi, N, scale, stream);
     else        launch_bwd<64, false>(Q, Kp, Vp, Op, lse, dOp, dQp, dKp, dVp, delta, BHi, N, scale, stream);
   }
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int N,
+                      int d, float scale, int causal, hipStream_t stream) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, false, B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  dispatch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices];     // each device's address of `scratch`, looked up on first use
+}  // namespace
+
+// The address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+static int scratch_of_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return FA_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return FA_ERR_DEVICE;
+    }
+    g_scratch[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return FA_OK;
+}
+
+extern "C" int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                              float scale, int causal, hipStream_t stream) {
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, true, B, H, N, d, scale, causal);
+  if (st != FA_OK) return st;
+  float* delta = nullptr;
+  const int sd = scratch_of_current_device(&delta);
+  if (sd != FA_OK) return sd;
+  // D is overwritten by the first kernel before anything reads it: nothing to clear
+  dispatch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

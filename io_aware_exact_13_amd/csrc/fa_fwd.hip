@@ -825,6 +825,8 @@ extern "C" const char* fa_status_str(int status) {
     case FA_ERR_FLAG: return "causal must be 0 or 1";
     case FA_ERR_ALIAS: return "output buffers overlap an input or each other";
     case FA_ERR_SPLITS: return "n_splits must be between 1 and 64";
+    case FA_ERR_SCRATCH: return "B*H*N exceeds the library's own workspace (FA_NOALLOC_ROWS rows)";
+    case FA_ERR_DEVICE: return "the current device or the address of the library's workspace is unavailable";
     default: return "unknown status";
   }
 }

@@ -25,7 +25,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_fa1order", "fa_fwd_fp8", "fa_fwd_fp8_tile",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_fa1order", "fa_fwd_fp8", "fa_fwd_fp8_tile",
                                     "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_fwd_tile", "fa_quant_fp8",
                                     "fa_status_str"]
 
@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     codes = [fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_HEAD_DIM, fa.FA_ERR_SCALE,
-             fa.FA_ERR_ALIGN, fa.FA_ERR_LAUNCH, fa.FA_ERR_FLAG, fa.FA_ERR_ALIAS, fa.FA_ERR_SPLITS]
+             fa.FA_ERR_ALIGN, fa.FA_ERR_LAUNCH, fa.FA_ERR_FLAG, fa.FA_ERR_ALIAS, fa.FA_ERR_SPLITS,
+             fa.FA_ERR_SCRATCH, fa.FA_ERR_DEVICE]
     names = [fa.fa_status_str(c) for c in codes]
     assert names[0] == "ok"
     assert len(set(names)) == len(names)
@@ -111,6 +112,23 @@ def call_bwd(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DL, 
 ])
 def test_bad_bwd_arguments_are_rejected_on_the_host(lib, kw, code):
     assert call_bwd(**kw) == code
+
+
+def call_bwd_noalloc(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, B=1, H=1, N=16, d=64,
+                    scale=0.125, causal=0):
+    return fa.fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_NULL), (dict(dv=0), fa.FA_ERR_NULL), (dict(N=0), fa.FA_ERR_SHAPE),
+    (dict(d=96), fa.FA_ERR_HEAD_DIM), (dict(scale=float("inf")), fa.FA_ERR_SCALE), (dict(causal=2), fa.FA_ERR_FLAG),
+    (dict(dq=DQ + 8), fa.FA_ERR_ALIGN), (dict(dq=Q), fa.FA_ERR_ALIAS), (dict(dk=DQ + 16), fa.FA_ERR_ALIAS),
+    (dict(N=fa.NOALLOC_ROWS + 1), fa.FA_ERR_SCRATCH), (dict(B=2, H=3, N=fa.NOALLOC_ROWS // 4), fa.FA_ERR_SCRATCH),
+])
+def test_bad_bwd_noalloc_arguments_are_rejected_on_the_host(lib, kw, code):
+    """The no-allocation backward checks what fa_bwd checks, and refuses
+    B*H*N beyond its own workspace, before any HIP call."""
+    assert call_bwd_noalloc(**kw) == code
 
 
 # fa_fwd_splitkv: fake addresses; every call is rejected on the host.

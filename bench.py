@@ -357,6 +357,54 @@ def gemm_calibration(m, steps, warmup, warm_s):
                       "frac_of_peak": round(tf / acc.PEAK_BF16_DENSE_TFLOPS, 4)}), flush=True)
 
 
+def ab_compare(w, variants, steps, reps, warm_s):
+    """Time fa_fwd of several builds of the library on the same inputs in one
+    process: each build is loaded through its own handle, and the builds take
+    turns, `reps` rounds of (warm_s seconds of untimed calls, then `steps`
+    timed calls on HIP events).  Prints one JSON line with TFLOP/s per build
+    and round."""
+    import ctypes
+    import torch
+    import workloads
+    from io_aware_exact_13_amd import accounting as acc
+    from io_aware_exact_13_amd.build import lib_path
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    libs = {}
+    for name in variants:
+        lib = ctypes.CDLL(lib_path(None if name == "default" else name))
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+        lib.fa_fwd.restype = ci
+        libs[name] = lib
+    flops = acc.attention_flops(w.B, w.H, w.N, w.d, w.causal)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H, w.N, w.d,
+            ctypes.c_float(w.scale), int(w.causal), stream.cuda_stream)
+    res = {name: [] for name in libs}
+    for r in range(reps):
+        for name, lib in libs.items():
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < warm_s:
+                for _ in range(4):
+                    if lib.fa_fwd(*args) != 0:
+                        raise RuntimeError(f"{name}: fa_fwd failed")
+                torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(steps):
+                lib.fa_fwd(*args)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / steps
+            res[name].append(round(flops / (ms * 1e-3) / 1e12, 1))
+            log(f"[ab] {w.name} round {r} {name:10s} {ms * 1e3:9.1f} us  {res[name][-1]:7.1f} TFLOP/s")
+    print(json.dumps({"metric": "fa_fwd TFLOP/s per build (same inputs, interleaved)", "workload": w.name,
+                      "steps": steps, "warm_s": warm_s, "results": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +428,10 @@ def main():
     ap.add_argument("--fp8", action="store_true", help="measure the FP8 forward fa_fwd_fp8 instead of fa_fwd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy 3 times (counter calibration)")
+    ap.add_argument("--ab", default=None, metavar="V1,V2,...",
+                    help="only compare builds of the forward (names from build.py TILE_VARIANTS, or 'default') "
+                         "on the same inputs in one process, interleaved over --reps rounds")
+    ap.add_argument("--reps", type=int, default=2, help="rounds of --ab")
     ap.add_argument("--gemm-calibration", type=int, default=0, metavar="M",
                     help="only time a plain bf16 M x M x M matrix product (torch.matmul, the vendor GEMM "
                          "library) on N(0,1) inputs: the MFMA rate this GPU sustains on a dense contraction")
@@ -409,6 +461,14 @@ def main():
         return
     if args.gemm_calibration:
         gemm_calibration(args.gemm_calibration, args.steps, args.warmup, args.warm_s)
+        return
+    if args.ab:
+        if args.shape:
+            B, H, N, d, causal = (int(x) for x in args.shape.split(","))
+            w = workloads.custom(B, H, N, d, bool(causal), seed=3)
+        else:
+            w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+        ab_compare(w, args.ab.split(","), args.steps, args.reps, max(args.warm_s, 0.3))
         return
 
     if args.shape:

@@ -40,6 +40,12 @@ TILE_VARIANTS = {
     "ahead1": ["-DFA_OPERAND_AHEAD=1"],    # MFMA operands requested one step pair ahead
     "ahead3": ["-DFA_OPERAND_AHEAD=3"],    # three step pairs ahead
     "exactmax": ["-DFA_EXACT_MAX=1"],      # reference maximum = running row maximum (no lag)
+    "noshare": ["-DFA_LAG_SHARE=0"],       # lag bounded by size only (no share-of-sum rule)
+    "share50": ["-DFA_LAG_SHARE=0.5f"],    # share-of-sum rule at 1/2
+    "share12": ["-DFA_LAG_SHARE=0.125f"],  # share-of-sum rule at 1/8
+    "d64max0": ["-DFA_D64_MAX_TILES=0"],   # d = 64: no row maximum from the first tile on
+    "d64max16": ["-DFA_D64_MAX_TILES=16"],  # d = 64: the row maximum on the first 16 tiles
+    "d64maxall": ["-DFA_D64_MAX_TILES=1000000"],  # d = 64: the row maximum on every tile
     "racecheck": ["-DFA_EXTRA_BARRIER=1"],  # a wait and a workgroup barrier after every step's LDS reads
 }
 TEST_VARIANTS = ("exactmax", "racecheck")

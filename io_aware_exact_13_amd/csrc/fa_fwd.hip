@@ -118,8 +118,28 @@ constexpr float kLn2 = 0.6931471805599453f;
 #ifndef FA_EXTRA_BARRIER
 #define FA_EXTRA_BARRIER 0
 #endif
+// The lag is bounded two ways.  (a) Size: P stays <= 2^kSlack (d = 128) and
+// a lane's tile sum <= kPMax (d = 64).  (b) Share: a key whose weight against
+// the lagging reference would exceed kShare of the row's sum so far moves
+// the reference to the true maximum (FA_LAG_SHARE = 0 turns this off).  Every
+// weight rounded to bf16 is then either <= 1 (at most the reference key's,
+// which is exactly 1) or less than kShare of its row's final sum, so the
+// rounding of one large weight adds at most 2^-8 kShare max|v| to |O|; with
+// the true maximum itself as reference (the online softmax as written) the
+// largest weight is 1 and exact.
+#ifndef FA_LAG_SHARE
+#define FA_LAG_SHARE 0.25f
+#endif
 constexpr float kPMax = 4294967296.0f;   // 2^32: largest tile sum of P a lane may reach before the reference moves
 constexpr float kSlack = FA_EXACT_MAX ? 0.0f : 8.0f;    // log2 units the reference max may lag the true max
+constexpr float kShare = FA_LAG_SHARE;   // largest share of the row's sum a lagged weight may take (0: no limit)
+// d = 64 forms no row maximum on most tiles (softmax_tile_lagged), but the
+// first FA_D64_MAX_TILES tiles of a workgroup's range take the row maximum
+// (softmax_tile): there the row's sum is still small, so the share rule would
+// make the no-maximum path recompute most tiles.
+#ifndef FA_D64_MAX_TILES
+#define FA_D64_MAX_TILES 8
+#endif
 
 // LDS geometry: unpadded rows with XOR-swizzled 16-byte chunks, so a tile is
 // exactly 16 KiB (d=128) and every wave copies the same number of 1 KiB
@@ -215,7 +235,16 @@ struct RowState {
   f32x16 acc[D / 32];   // O^T accumulators: lane holds column (r/4)*8 + 4h + r%4 of each 32-col tile
   float m_ref;          // reference max, log2 units of the scaled score
   float l_part;         // this lane's share of the exponential sum
+  float slack;          // how far (log2 units) the tile maximum may pass m_ref before the reference moves
 };
+
+// The slack the share rule allows for a row whose exponential sum so far is
+// l_row: the new maximum's weight 2^slack must stay <= kShare l_row, and
+// <= 2^kSlack.  0 before the first key (l_row = 0: any finite maximum moves
+// the reference).
+__device__ __forceinline__ float share_slack(float l_row) {
+  return fminf(kSlack, fmaxf(0.f, __builtin_amdgcn_logf(l_row) + __builtin_log2f(kShare)));
+}
 
 // S^T = K Q^T for one tile (fp32, unscaled), not overlapped with anything
 // (used once, for S_0).  A operand: K row 32 kb + l32, columns 16 ks + 8 h
@@ -255,7 +284,13 @@ __device__ __forceinline__ bf16x8 v_operand(const char* Vt, int v_off_ct, int t)
 // P = exp2(S * c - m) in bf16, row sum in fp32.  Returns alpha, the factor
 // the accumulators must be multiplied by (1 unless the reference moved), and
 // sets *rescale when some lane of the wave needs it.
-template <int D, bool MASKED>
+//
+// The slack follows the share rule (kShare): it is set from the row's sum at
+// REFRESH steps (the first of every four) and drops to 0 for a row whose
+// reference moved, until the next refresh.  The row's sum only grows while
+// the reference stays, so a slack taken from an earlier, smaller sum is
+// still within the rule.
+template <int D, bool MASKED, bool REFRESH>
 __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, int lim, int h, float c_log2,
                                               RowState<D>& st, bf16x8 (&pf)[kBC / 16], bool* rescale) {
   constexpr int kKb = kBC / 32;
@@ -290,7 +325,13 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, i
     n = m;
   }
   const float m_tile = max_halves(part[0]) * c_log2;
-  const bool grow = m_tile > st.m_ref + kSlack;
+  // the reference moves when the tile's maximum passes it by more than the
+  // slack: kSlack, or (share rule) so much that the new maximum's weight
+  // 2^(m_tile - m_ref) would pass kShare of the row's sum
+  constexpr bool kRule = kShare > 0.f && !FA_EXACT_MAX;
+  if constexpr (kRule && REFRESH) st.slack = share_slack(sum_halves(st.l_part));
+  const bool grow = m_tile > st.m_ref + (kRule ? st.slack : kSlack);
+  if constexpr (kRule) st.slack = grow ? 0.f : st.slack;
   const float m_new = grow ? m_tile : st.m_ref;
   *rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
   // 0 while the row has seen no key (acc and l are still 0): no exp2 of
@@ -345,7 +386,7 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[kBC / 32], float c_l
 // reference (softmax_redo); *lt receives this lane's tile sum.
 template <bool MASKED>
 __device__ __forceinline__ bool softmax_tile_lagged(f32x16 (&s)[kBC / 32], int key0, int lim, int h, float c_log2,
-                                             float m_ref, bf16x8 (&pf)[kBC / 16], float* lt) {
+                                             float m_ref, float l_part, bf16x8 (&pf)[kBC / 16], float* lt) {
   constexpr int kKb = kBC / 32;
   if (MASKED) {
 #pragma unroll
@@ -364,7 +405,12 @@ __device__ __forceinline__ bool softmax_tile_lagged(f32x16 (&s)[kBC / 32], int k
   for (int t = 0; t < kBC / 16; ++t) asm volatile("" : "+v"(pf[t]));
   asm volatile("" : "+v"(sum));
   *lt = sum;
-  return __builtin_amdgcn_ballot_w64(!(sum <= kPMax)) != 0;
+  // accepted: every P of the lane is <= its tile sum, which is <= 1 (no
+  // weight above the reference key's) or <= kShare of the lane's share of
+  // the row's sum so far, and <= kPMax
+  float limit = kPMax;
+  if constexpr (kShare > 0.f) limit = fminf(kPMax, fmaxf(1.f, kShare * l_part));
+  return __builtin_amdgcn_ballot_w64(!(sum <= limit)) != 0;
 }
 
 // The rare path of softmax_tile: the row maximum of the (masked) tile, the
@@ -433,7 +479,7 @@ struct Ctx {
 // The LDS buffers read and the ones being filled are distinct restrict
 // pointers: the compiler then keeps the copies in flight across the reads
 // (the next step's explicit wait orders them).
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool NOMAX, bool REFRESH>
 __device__ __forceinline__ void step(const char* __restrict__ k_read, const char* __restrict__ v_read,
                                      char* __restrict__ k_fill, char* __restrict__ v_fill, const Ctx<D>& c,
                                      int j, const bf16x8 (&qf)[D / 16], f32x16 (&s_in)[kBC / 32],
@@ -483,13 +529,15 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
     mfma(i);
     if (i % kCopyEvery == 1) copy(i / kCopyEvery);
   }
-  // d = 64: the lagged reference without a row maximum (about 5% faster
-  // there; no gain for d = 128, whose MFMA work per tile hides the max tree)
-  constexpr bool kNoMax = (D == 64) && !FA_EXACT_MAX;
+  // NOMAX (d = 64 past its first tiles): the lagged reference without a row
+  // maximum (about 5% faster there; no gain for d = 128, whose MFMA work per
+  // tile hides the max tree)
+  constexpr bool kNoMax = NOMAX && !FA_EXACT_MAX;
   bool rescale = false;
   float alpha = 1.f, lt = 0.f;
-  if constexpr (kNoMax) rescale = softmax_tile_lagged<MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st.m_ref, p_out, &lt);
-  else alpha = softmax_tile<D, MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st, p_out, &rescale);
+  if constexpr (kNoMax)
+    rescale = softmax_tile_lagged<MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st.m_ref, st.l_part, p_out, &lt);
+  else alpha = softmax_tile<D, MASKED, REFRESH>(s_in, j * kBC, c.lim, c.h, c.c_log2, st, p_out, &rescale);
   // Interleave: each step pair is two MFMAs, its operand reads and an equal
   // share of the softmax's VALU work between and after them (mask 0x008
   // MFMA, 0x100 LDS read, 0x002 VALU, 0x010 VMEM).
@@ -530,28 +578,31 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
 // Four steps, one turn of the LDS rings, S/P register sets swapped between
 // steps.  Step j reads K_{j+1} from K buffer (j+1)%4 and V_{j-1} from V
 // buffer (j-1)%4, and fills K buffer (j+3)%4 and V buffer (j+1)%4.
-template <int D, bool MASKED, int PH>
+// The share rule's slack is refreshed at the first step of every four.
+template <int D, bool MASKED, int PH, bool NOMAX = false>
 __device__ __forceinline__ void step_at(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
                                         f32x16 (&sa)[kBC / 32], f32x16 (&sb)[kBC / 32],
                                         bf16x8 (&pa)[kBC / 16], bf16x8 (&pb)[kBC / 16], RowState<D>& st) {
   using G = Geom<D>;
   constexpr int R = G::kRing;
   if constexpr (PH % 2 == 0)
-    step<D, MASKED>(c.lds + G::k_buf((PH + 1) % R), c.lds + G::v_rel((PH + R - 1) % R),
-                    c.lds + G::k_buf((PH + 3) % R), c.lds + G::v_buf((PH + 1) % R), c, j, qf, sa, sb, pa, pb, st);
+    step<D, MASKED, NOMAX, PH == 0>(c.lds + G::k_buf((PH + 1) % R), c.lds + G::v_rel((PH + R - 1) % R),
+                                    c.lds + G::k_buf((PH + 3) % R), c.lds + G::v_buf((PH + 1) % R), c, j, qf, sa,
+                                    sb, pa, pb, st);
   else
-    step<D, MASKED>(c.lds + G::k_buf((PH + 1) % R), c.lds + G::v_rel((PH + R - 1) % R),
-                    c.lds + G::k_buf((PH + 3) % R), c.lds + G::v_buf((PH + 1) % R), c, j, qf, sb, sa, pb, pa, st);
+    step<D, MASKED, NOMAX, PH == 0>(c.lds + G::k_buf((PH + 1) % R), c.lds + G::v_rel((PH + R - 1) % R),
+                                    c.lds + G::k_buf((PH + 3) % R), c.lds + G::v_buf((PH + 1) % R), c, j, qf, sb,
+                                    sa, pb, pa, st);
 }
 
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool NOMAX = false>
 __device__ __forceinline__ void step_quad(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
                                           f32x16 (&sa)[kBC / 32], f32x16 (&sb)[kBC / 32],
                                           bf16x8 (&pa)[kBC / 16], bf16x8 (&pb)[kBC / 16], RowState<D>& st) {
-  step_at<D, MASKED, 0>(c, j, qf, sa, sb, pa, pb, st);
-  step_at<D, MASKED, 1>(c, j + 1, qf, sa, sb, pa, pb, st);
-  step_at<D, MASKED, 2>(c, j + 2, qf, sa, sb, pa, pb, st);
-  step_at<D, MASKED, 3>(c, j + 3, qf, sa, sb, pa, pb, st);
+  step_at<D, MASKED, 0, NOMAX>(c, j, qf, sa, sb, pa, pb, st);
+  step_at<D, MASKED, 1, NOMAX>(c, j + 1, qf, sa, sb, pa, pb, st);
+  step_at<D, MASKED, 2, NOMAX>(c, j + 2, qf, sa, sb, pa, pb, st);
+  step_at<D, MASKED, 3, NOMAX>(c, j + 3, qf, sa, sb, pa, pb, st);
 }
 
 // SPLIT: the workgroup covers one of n_splits contiguous ranges of its query
@@ -673,6 +724,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int ct = 0; ct < kCt; ++ct) st.acc[ct] = f32x16{};
   st.m_ref = -INFINITY;
   st.l_part = 0.f;
+  st.slack = 0.f;
   f32x16 sa[kBC / 32], sb[kBC / 32];
   bf16x8 pa[kBC / 16], pb[kBC / 16];
 #pragma unroll
@@ -686,11 +738,17 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // j - j0 modulo 4) are constants
   int j = j0;
   const int j_fast = max(j0, j_mask);                   // tiles [j0, j_fast) need no mask
-  for (; j + 4 <= j_fast; j += 4) step_quad<D, false>(c, j, qf, sa, sb, pa, pb, st);
-  for (; j + 4 <= c.n_tiles; j += 4) step_quad<D, true>(c, j, qf, sa, sb, pa, pb, st);
-  if (j < c.n_tiles) step_at<D, true, 0>(c, j++, qf, sa, sb, pa, pb, st);
-  if (j < c.n_tiles) step_at<D, true, 1>(c, j++, qf, sa, sb, pa, pb, st);
-  if (j < c.n_tiles) step_at<D, true, 2>(c, j++, qf, sa, sb, pa, pb, st);
+  // d = 64: the row maximum on the first FA_D64_MAX_TILES tiles, none after
+  constexpr bool kNoMax = D == 64;
+  if constexpr (kNoMax) {
+    const int j_max = min(j_fast, j0 + FA_D64_MAX_TILES);
+    for (; j + 4 <= j_max; j += 4) step_quad<D, false, false>(c, j, qf, sa, sb, pa, pb, st);
+  }
+  for (; j + 4 <= j_fast; j += 4) step_quad<D, false, kNoMax>(c, j, qf, sa, sb, pa, pb, st);
+  for (; j + 4 <= c.n_tiles; j += 4) step_quad<D, true, kNoMax>(c, j, qf, sa, sb, pa, pb, st);
+  if (j < c.n_tiles) step_at<D, true, 0, kNoMax>(c, j++, qf, sa, sb, pa, pb, st);
+  if (j < c.n_tiles) step_at<D, true, 1, kNoMax>(c, j++, qf, sa, sb, pa, pb, st);
+  if (j < c.n_tiles) step_at<D, true, 2, kNoMax>(c, j++, qf, sa, sb, pa, pb, st);
   // ---- O += V_{n-1} P_{n-1}: V_{n-1} is in ring buffer (n-1-j0) % 4
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();

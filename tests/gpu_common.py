@@ -47,20 +47,15 @@ def bf16_half_ulp(x):
     return np.exp2(np.floor(np.log2(ax)) - 8.0)
 
 
-def compare_full(q, k, v, scale, causal, o, lse, with_rounding=False, p_rounding=False):
+def compare_full(q, k, v, scale, causal, o, lse, with_rounding=False):
     """max|dO|, mean|dO|, max|dLSE| against the oracle.  With with_rounding, the
     first value is max(|dO| - half a bf16 ulp of the oracle's O): the part of
-    the error not explained by O being stored in bf16.  With p_rounding as
-    well, 2^-8 |O| more is set aside: in a row dominated by one key, O is
-    that key's bf16-rounded weight (relative error up to 2^-8) times its V row
-    over the fp32 sum of the weights, so |O| 2^-8 of error comes from the
-    rounding of P that the method prescribes before the P V product."""
+    the error not explained by O being stored in bf16."""
     ro, rl = oracle.attention(to64(q), to64(k), to64(v), scale, causal)
     do = np.abs(to64(o) - ro)
     dl = np.abs(to64(lse) - rl)
     if with_rounding:
-        allowance = bf16_half_ulp(ro) + (2.0 ** -8 * np.abs(ro) if p_rounding else 0.0)
-        return float((do - allowance).max()), do.mean(), dl.max(), do.max()
+        return float((do - bf16_half_ulp(ro)).max()), do.mean(), dl.max(), do.max()
     return do.max(), do.mean(), dl.max()
 
 

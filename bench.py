@@ -314,8 +314,20 @@ def cpu_baseline(w, n_heads=32, backward=False):
     flops = 4.0 * w.N * w.N * w.d * n_heads / (2.0 if w.causal else 1.0) * (2.5 if backward else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(), "usable_cores": usable_cores(), "blas_threads": int(threads),
+            "seconds": round(dt, 2),
             "sample": f"{n_heads} of {w.B * w.H} heads of {w.name} (all {w.N} query rows each), "
                       f"{'gradients, ' if backward else ''}fp64 numpy, {dt:.1f} s"}
+
+
+def oracle_table():
+    """Time the oracle as it stands (fp64 numpy, heads one after another, the
+    host's BLAS threads) over every head of every named workload; one JSON
+    line per workload."""
+    import workloads
+    for name in workloads.WORKLOAD_ORDER:
+        w = workloads.WORKLOADS[name]
+        r = cpu_baseline(w, n_heads=w.B * w.H)
+        print(json.dumps({"workload": name, **r}), flush=True)
 
 
 def gemm_calibration(m, steps, warmup, warm_s):
@@ -432,6 +444,8 @@ def main():
                     help="only compare builds of the forward (names from build.py TILE_VARIANTS, or 'default') "
                          "on the same inputs in one process, interleaved over --reps rounds")
     ap.add_argument("--reps", type=int, default=2, help="rounds of --ab")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="only time the CPU oracle over every head of every named workload (no GPU work)")
     ap.add_argument("--gemm-calibration", type=int, default=0, metavar="M",
                     help="only time a plain bf16 M x M x M matrix product (torch.matmul, the vendor GEMM "
                          "library) on N(0,1) inputs: the MFMA rate this GPU sustains on a dense contraction")
@@ -445,6 +459,9 @@ def main():
     import workloads
     from io_aware_exact_13_amd import accounting as acc
 
+    if args.oracle_table:            # CPU only
+        oracle_table()
+        return
     if args.lib:
         fa.use_library(args.lib)
     if not torch.cuda.is_available():

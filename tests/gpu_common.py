@@ -189,3 +189,37 @@ def fp8_flip_allowance(q, k, v, scale, causal, rows):
     for c0 in range(0, n, 512):
         top = np.maximum(top, (w[:, c0:c0 + 512, None] * av[None, c0:c0 + 512, :]).max(axis=1))
     return 2.0 ** -3 * top + 2.0 ** -9 * av.max(axis=0)[None, :] / l
+
+
+def e4m3_p_bounds(q, k, v, scale, causal, rows):
+    """What rounding P to E4M3 before P V can move O, from the plain
+    definition alone (no key blocking): for the given rows of one head
+    (fp64 operands [N, d]), returns (the exact O, the exact LSE, a per-element
+    bound on |O_fp8 - O|, the per-element variance of that difference under
+    independent round-to-nearest errors).
+
+    Whatever reference a blocked softmax rounds P against, that reference is
+    at most the row's final maximum, so key j's rounded weight P_j and the
+    factor alpha_j its block is later rescaled by satisfy alpha_j P_j =
+    w_j l (w_j its final softmax weight, l = sum_j exp(s_j - max_j s_j)) with
+    alpha_j <= 1.  E4M3 rounds a normal P (>= 2^-6) with error at most 2^-4 P
+    and a smaller one with error at most 2^-10, so key j moves O_c by at most
+    max(2^-4 w_j, 2^-10 / l) |v_jc|; the bound sums that over the keys, and
+    the variance takes each error uniform over its range (variance a^2 / 3
+    for error at most a)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    n = k.shape[0]
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        s = np.where(np.arange(n)[None, :] > rows[:, None], -np.inf, s)
+    mx = s.max(axis=1, keepdims=True)
+    e = np.exp(s - mx)
+    l = e.sum(axis=1, keepdims=True)
+    w = e / l
+    o = w @ v
+    lse = mx[:, 0] + np.log(l[:, 0])
+    visible = np.isfinite(s).astype(np.float64)
+    a = np.maximum(2.0 ** -4 * w, visible * (2.0 ** -10) / l)
+    bound = a @ np.abs(v)
+    var = (a * a) @ (v * v) / 3.0
+    return o, lse, bound, var

@@ -19,7 +19,7 @@ import torch
 import io_aware_exact_13_amd as fa
 import oracle
 import workloads
-from gpu_common import announce, bf16_half_ulp, device, fp8_flip_allowance, to64
+from gpu_common import announce, bf16_half_ulp, device, e4m3_p_bounds, fp8_flip_allowance, to64
 from oracle import fp8 as ofp8
 
 pytestmark = pytest.mark.gpu
@@ -141,6 +141,50 @@ def test_fp8_attention_matches_oracle(B, H, N, d, causal):
     assert worst <= 0 and mean <= O_MEAN_EXCESS and dl <= LSE_MAX
 
 
+def check_rows_against_plain(qq, kk, vv, scale, causal, o, lse, picks):
+    """The GPU's O/LSE on (b, h, rows) picks against the plain definition on
+    the dequantised operands (no key blocking anywhere), with the E4M3
+    rounding of P bounded from that definition alone (gpu_common.e4m3_p_bounds).
+    Returns (max of |dO| - bar, observed / predicted mean square of dO, max |dLSE|)."""
+    worst, worst_l, sq, pred = -np.inf, 0.0, 0.0, 0.0
+    deq = [ofp8.dequantize_heads(c, s) for c, s in (qq, kk, vv)]
+    for b, h, rows in picks:
+        qd, kd, vd = (x[b, h] for x in deq)
+        ro, rl, bound, var = e4m3_p_bounds(qd, kd, vd, scale, causal, rows)
+        go = to64(o[b, h, torch.as_tensor(rows)])
+        gl = to64(lse[b, h, torch.as_tensor(rows)])
+        diff = np.abs(go - ro)
+        half = bf16_half_ulp(ro)
+        worst = max(worst, float((diff - (half + bound + 1e-5)).max()))
+        worst_l = max(worst_l, float(np.abs(gl - rl).max()))
+        sq += float((diff * diff).sum())
+        pred += float((var + half * half / 3.0).sum())
+    return worst, sq / pred, worst_l
+
+
+PLAIN_CASES = [(1, 2, 513, 128, True), (1, 1, 4096, 128, True), (1, 1, 2048, 64, False), (2, 2, 333, 64, True)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", PLAIN_CASES)
+def test_fp8_attention_within_the_e4m3_bound_of_the_plain_definition(B, H, N, d, causal):
+    """A check that does not depend on how the kernel blocks the keys: O
+    against the plain softmax attention of the dequantised operands, within
+    the most that rounding P to E4M3 can move it (a change of the kernel's
+    key blocking must still pass this, and a wrong rounding or a lost term
+    must not), and the mean square difference at most what independent
+    roundings with errors spread over their whole range would give."""
+    w = workloads.custom(B, H, N, d, causal, seed=6400 + N + d + int(causal))
+    q, k, v = workloads.make_inputs(w)
+    rotate = d == 128
+    qq, kk, vv = oracle_quant(q, k, v, rotate, workloads.make_fp8_signs(w.seed, d))
+    announce(f"[fp8-plain] {w.name} rotate={rotate}")
+    o, lse = gpu_fwd_fp8(qq, kk, vv, w.scale, causal)
+    picks = [(b, h, np.arange(N)) for b in range(B) for h in range(H)]
+    worst, ratio, dl = check_rows_against_plain(qq, kk, vv, w.scale, causal, o, lse, picks)
+    announce(f"    |dO| - bound {worst:.3e}  mean square / predicted {ratio:.3f}  max|dLSE| {dl:.3e}")
+    assert worst <= 0 and ratio <= 1.0 and dl <= LSE_MAX
+
+
 def test_fp8_headline_shape_on_sampled_rows():
     """1 x 32 x 16384 x 128, causal: the GPU quantises all heads (two checked
     bit for bit against the oracle), the GPU forward runs on its codes, and
@@ -173,6 +217,10 @@ def test_fp8_headline_shape_on_sampled_rows():
         worst, mean, dl = check_rows(qq, kk, vv, w.scale, True, o[:, h:h + 1], lse[:, h:h + 1], [(0, 0, rows)])
         announce(f"    excess over bar {worst:.3e}  mean excess {mean:.3e}  max|dLSE| {dl:.3e}")
         assert worst <= 0 and mean <= O_MEAN_EXCESS and dl <= LSE_MAX
+        worst, ratio, dl = check_rows_against_plain(qq, kk, vv, w.scale, True, o[:, h:h + 1], lse[:, h:h + 1],
+                                                     [(0, 0, rows)])
+        announce(f"    plain definition: |dO| - bound {worst:.3e}  mean square / predicted {ratio:.3f}")
+        assert worst <= 0 and ratio <= 1.0 and dl <= LSE_MAX
 
 
 @pytest.mark.parametrize("name", ["causal_peaky_b1h8_n65536_d128", "short_b16h32_n2048_d64",

@@ -46,6 +46,9 @@ TILE_VARIANTS = {
     "d64max0": ["-DFA_D64_MAX_TILES=0"],   # d = 64: no row maximum from the first tile on
     "d64max16": ["-DFA_D64_MAX_TILES=16"],  # d = 64: the row maximum on the first 16 tiles
     "d64maxall": ["-DFA_D64_MAX_TILES=1000000"],  # d = 64: the row maximum on every tile
+    "valu2": ["-DFA_VALU_PER_MFMA=2"],     # softmax VALU instructions placed after each MFMA: 2
+    "valu4": ["-DFA_VALU_PER_MFMA=4"],     # 4
+    "valu5": ["-DFA_VALU_PER_MFMA=5"],     # 5 (all of a d = 128 step's softmax between its MFMAs)
     "racecheck": ["-DFA_EXTRA_BARRIER=1"],  # a wait and a workgroup barrier after every step's LDS reads
 }
 TEST_VARIANTS = ("exactmax", "racecheck")

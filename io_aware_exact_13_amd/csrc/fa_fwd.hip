@@ -89,6 +89,11 @@ constexpr int kBC = 64;           // keys per K/V tile
 #ifndef FA_OPERAND_AHEAD
 #define FA_OPERAND_AHEAD 2
 #endif
+// VALU instructions of the softmax the scheduler places after each MFMA of a
+// step (the rest follow the step's last MFMA).
+#ifndef FA_VALU_PER_MFMA
+#define FA_VALU_PER_MFMA 3
+#endif
 // Waves per workgroup (32 query rows each): 8 at d = 128 (one workgroup per
 // CU, 128 KiB of LDS), 4 at d = 64 (64 KiB, two workgroups per CU, whose
 // waves share the SIMDs and drift apart).
@@ -546,10 +551,10 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   for (int i = 0; i < kPV; ++i) {
     if (i + kAhead < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, FA_VALU_PER_MFMA, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i % kCopyEvery == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, FA_VALU_PER_MFMA, 0);
   }
   if constexpr (FA_EXTRA_BARRIER) {
     __builtin_amdgcn_sched_barrier(0);

@@ -106,8 +106,14 @@ int fa_fwd_tile(int B, int H, int N, int d, int causal,
  *
  * Arguments: q, k, v, o, lse, B, H, N, d, scale, causal, stream as for fa_fwd
  * (same results up to fp32 rounding order), and
- *   n_splits  1 .. 64 key ranges per query block (ranges may be empty when a
- *             block has fewer key tiles than n_splits; they contribute nothing).
+ *   n_splits  1 .. 64: the key ranges of every query block, or, under the
+ *             causal mask when fa_fwd_splitkv_ranges says so, at most: query
+ *             block b (of Nb = ceil(N / rows_per_block)) is then cut into
+ *             ceil((b + 1) / r) ranges, r = ceil(Nb / n_splits), so that
+ *             every range holds about the same number of key tiles.  Ranges
+ *             may be empty when a block has fewer key tiles than ranges;
+ *             they contribute nothing.  Workspace entries of ranges a block
+ *             does not have are neither written nor read.
  *   o_part    fp32 workspace [n_splits][B][H][N][d], 16-byte aligned.
  *   lse_part  fp32 workspace [n_splits][B][H][N], 4-byte aligned.
  * Both workspaces are overwritten; outputs and workspaces must not overlap
@@ -123,11 +129,25 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  * about two rounds of the workgroups the GPU runs at once (one per compute
  * unit at d = 128, two at d = 64; 1 when fa_fwd alone fills two rounds, or
  * when the ranges would hold fewer than 8 key tiles of 64), at most 16, and the
- * workspace bytes fa_fwd_splitkv needs for it.  Any output pointer may be
+ * workspace bytes fa_fwd_splitkv needs for it.  The count is the one with
+ * the smallest time in the model fa_fwd_splitkv_ranges describes, each count
+ * with its own range rule; 1 when fa_fwd alone fills two rounds.  Any output pointer may be
  * NULL.  Returns FA_OK or the FA_ERR_* code fa_fwd would return.  Host only.
  */
 int fa_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int* n_splits,
                         size_t* o_part_bytes, size_t* lse_part_bytes);
+
+/*
+ * fa_fwd_splitkv_ranges -- the range rule fa_fwd_splitkv uses for n_splits:
+ * *r_units = 0 when every query block is cut into n_splits ranges, or, under
+ * the causal mask, r > 0 when query block b is cut into ceil((b + 1) / r)
+ * ranges (r = ceil(blocks per head / n_splits)).  The library takes whichever
+ * its model of the launch (list scheduling of the workgroups over the compute
+ * units, plus the merge) predicts is faster; the choice depends only on the
+ * arguments.  Returns FA_OK or the FA_ERR_* code fa_fwd_splitkv would return
+ * for them.  Host only.
+ */
+int fa_fwd_splitkv_ranges(int B, int H, int N, int d, int causal, int n_splits, int* r_units);
 
 /*
  * fa_fwd_fa1order -- the same forward computed in the other loop order the

@@ -76,6 +76,8 @@ def load_library():
     lib.fa_fwd_splitkv_plan.argtypes = [ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_size_t),
                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_fwd_splitkv_plan.restype = ci
+    lib.fa_fwd_splitkv_ranges.argtypes = [ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci)]
+    lib.fa_fwd_splitkv_ranges.restype = ci
     lib.fa_fwd_fa1order.argtypes = [vp] * 5 + [ci, ci, ci, ci, ctypes.c_float, ci, vp, vp, vp, vp]
     lib.fa_fwd_fa1order.restype = ci
     u64 = ctypes.c_uint64
@@ -123,6 +125,16 @@ def fa_fwd_splitkv_plan(B, H, N, d, causal):
     if st != FA_OK:
         raise FaError(st, "fa_fwd_splitkv_plan")
     return n.value, ob.value, lb.value
+
+
+def fa_fwd_splitkv_ranges(B, H, N, d, causal, n_splits):
+    """The range rule fa_fwd_splitkv uses: 0 (n_splits ranges per query block)
+    or r > 0 (under the causal mask, ceil((b + 1) / r) ranges for block b)."""
+    r = ctypes.c_int()
+    st = load_library().fa_fwd_splitkv_ranges(B, H, N, d, int(causal), int(n_splits), ctypes.byref(r))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv_ranges")
+    return r.value
 
 
 def fa_fwd_fa1order(q, k, v, o, lse, B, H, N, d, scale, causal, o_acc, m, l, stream) -> int:

@@ -62,6 +62,11 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "fa.h"
 
 namespace {
@@ -106,6 +111,15 @@ __host__ __device__ constexpr int rows_per_block(int d) { return d == 64 ? kBROf
 __host__ __device__ constexpr int threads_per_block(int d) { return d == 64 ? kThreadsOf<64> : kThreadsOf<128>; }
 constexpr int kXcds = 8;          // accelerator dies; workgroups are dealt to them round-robin
 constexpr int kMaxSplits = 64;    // key ranges per query block in the split-KV forward
+
+// Split-KV under the causal mask: query block b (0-based) sees about b + 1
+// units of key tiles, and is cut into ceil((b + 1) / r) key ranges, so that
+// ranges hold about r units each whatever the block.  causal_units(k, r) is
+// the number of ranges of blocks 0 .. k-1: sum over i = 1 .. k of ceil(i / r)
+// = r q (q + 1) / 2 + (q + 1)(k - q r) with q = k / r.
+__host__ __device__ constexpr long long causal_units(long long k, long long r) {
+  return r * (k / r) * (k / r + 1) / 2 + (k / r + 1) * (k % r);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Reference maximum.  By default it lags the running row maximum (see
@@ -610,17 +624,19 @@ __device__ __forceinline__ void step_quad(const Ctx<D>& c, int j, const bf16x8 (
   step_at<D, MASKED, 3, NOMAX>(c, j + 3, qf, sa, sb, pa, pb, st);
 }
 
-// SPLIT: the workgroup covers one of n_splits contiguous ranges of its query
-// block's visible key tiles and writes an fp32 partial (O_s = acc / l over its
-// keys, LSE_s) to Opart / Lpart ([n_splits][B*H][N][d], [n_splits][B*H][N]);
-// fa_merge_kernel combines them.  Otherwise it covers all the tiles and
-// writes O (bf16) and LSE.
+// SPLIT: the workgroup covers one contiguous range of its query block's
+// visible key tiles and writes an fp32 partial (O_s = acc / l over its keys,
+// LSE_s) to Opart / Lpart ([n_splits][B*H][N][d], [n_splits][B*H][N]);
+// fa_merge_kernel combines them.  Without the mask every block has n_splits
+// ranges; under it, with r_units > 0, block b has ceil((b + 1) / r_units)
+// (causal_units), the longest blocks' ranges first.  Otherwise the workgroup
+// covers all the tiles and writes O (bf16) and LSE.
 template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                    float* __restrict__ Opart, float* __restrict__ Lpart,
-                   int BH, int N, int n_qblocks, int n_splits, float c_log2) {
+                   int BH, int N, int n_qblocks, int n_splits, int r_units, float c_log2) {
   using G = Geom<D>;
   constexpr int kDs = D / 16;
   constexpr int kCt = D / 32;
@@ -639,13 +655,30 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // heads, walked head by head, so the XCD's running workgroups share one
   // head's K/V stream in its L2.
   const int wg = blockIdx.x;
-  const int per_head = n_qblocks * (SPLIT ? n_splits : 1);
+  const bool kUnits = SPLIT && CAUSAL && r_units > 0;   // ranges in proportion to the block's length
+  const int per_head = kUnits ? (int)causal_units(n_qblocks, r_units) : n_qblocks * (SPLIT ? n_splits : 1);
   const int n_wg = BH * per_head;
   const int logical = (n_wg % kXcds == 0) ? (wg % kXcds) * (n_wg / kXcds) + wg / kXcds : wg;
   const int bh = logical / per_head;
-  const int qi = SPLIT ? (logical % per_head) / n_splits : logical % per_head;
-  const int split = SPLIT ? (logical % per_head) % n_splits : 0;
-  const int qb = CAUSAL ? (n_qblocks - 1 - qi) : qi;
+  int qb, split = 0, n_ranges = SPLIT ? n_splits : 1;
+  if (kUnits) {
+    // the w-th range of the head in block order, counted from the last
+    // (longest) block: the largest qb with causal_units(qb) <= w
+    const int w = per_head - 1 - logical % per_head;
+    int lo = 0, hi = n_qblocks;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (causal_units(mid, r_units) <= w) lo = mid;
+      else hi = mid;
+    }
+    qb = lo;
+    split = w - (int)causal_units(qb, r_units);
+    n_ranges = (qb + r_units) / r_units;
+  } else {
+    const int qi = SPLIT ? (logical % per_head) / n_splits : logical % per_head;
+    split = SPLIT ? (logical % per_head) % n_splits : 0;
+    qb = CAUSAL ? (n_qblocks - 1 - qi) : qi;
+  }
   constexpr int kBR = kBROf<D>;
   const int q0 = qb * kBR;
   const int qrow = q0 + c.wave * 32 + l32;   // this lane's query
@@ -663,8 +696,8 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   const int all_tiles = (kv_end + kBC - 1) / kBC;
   // this workgroup's tiles [j0, n_tiles): all of them, or one split's share
-  const int j0 = SPLIT ? (int)((long long)split * all_tiles / n_splits) : 0;
-  c.n_tiles = SPLIT ? (int)((long long)(split + 1) * all_tiles / n_splits) : all_tiles;
+  const int j0 = SPLIT ? (int)((long long)split * all_tiles / n_ranges) : 0;
+  c.n_tiles = SPLIT ? (int)((long long)(split + 1) * all_tiles / n_ranges) : all_tiles;
   c.kv_end = min(kv_end, c.n_tiles * kBC);              // copies past it read zeros, no traffic
   // tiles from j_mask on hold keys past the end or past some query of the block
   int j_mask = (N - 1) / kBC;                           // the tile holding key N-1
@@ -834,16 +867,19 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 // is the two-block merge of the online softmax ("为什么Flash Attention能将注意力
 // 计算提速数倍而不损失精度", 在线Softmax技巧) applied to n blocks at once, with
 // the blocks' statistics folded into their logsumexps.  D/8 lanes per row,
-// 8 columns each.
+// 8 columns each.  With r_units > 0 (under the causal mask) a row of query
+// block b has ceil((b + 1) / r_units) partials, else n_splits.
 template <int D>
 __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ Opart,
                                                        const float* __restrict__ Lpart, __bf16* __restrict__ O,
-                                                       float* __restrict__ LSE, long long rows, int n_splits) {
+                                                       float* __restrict__ LSE, long long rows, int N,
+                                                       int n_splits, int r_units) {
   constexpr int kLanes = D / 8;
   constexpr int kRows = 256 / kLanes;
   const long long row = (long long)blockIdx.x * kRows + threadIdx.x / kLanes;
   const int c0 = (threadIdx.x % kLanes) * 8;
   if (row >= rows) return;
+  if (r_units > 0) n_splits = ((int)(row % N) / kBROf<D> + r_units) / r_units;
   float m = -INFINITY;
   for (int sp = 0; sp < n_splits; ++sp) m = fmaxf(m, Lpart[(size_t)sp * rows + row]);
   float z = 0.f;
@@ -949,13 +985,82 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const dim3 grid((unsigned)blocks), block(threads_per_block(d));
   float* np = nullptr;
   if (d == 128) {
-    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
-    else        hipLaunchKernelGGL((fa_fwd_kernel<128, false, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
+    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, 1, c_log2);
+    else        hipLaunchKernelGGL((fa_fwd_kernel<128, false, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, 1, c_log2);
   } else {
-    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<64, true, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
-    else        hipLaunchKernelGGL((fa_fwd_kernel<64, false, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, c_log2);
+    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<64, true, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, 1, c_log2);
+    else        hipLaunchKernelGGL((fa_fwd_kernel<64, false, false>), grid, block, 0, stream, Q, Kp, Vp, Op, lse, np, np, BH, N, nqb, 1, 1, c_log2);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// A model of the split-KV forward's time, used to choose its ranges: list
+// scheduling of the workgroups, in dispatch order, onto the XCDs' compute
+// units (each XCD takes a contiguous run of the grid when the grid is a
+// multiple of 8, else every 8th workgroup), each costing its key tiles plus a
+// fixed overhead, then the merge's round trip of the fp32 partials.  The
+// constants were fitted to side-by-side measurements on one MI355X (causal
+// shares of 2 to 8 heads of 8K-16K tokens): per 64-key tile 1.35 us at
+// d = 128 and 0.40 us at d = 64 (two workgroups per CU, each at half speed),
+// 6 and 4 tiles of overhead per workgroup, and the merge at 8 TB/s plus 20 us.
+static double split_model_time(int B, int H, int N, int d, int causal, int n_splits, int r_units) {
+  const int br = rows_per_block(d);
+  const int nqb = (N + br - 1) / br;
+  const long long bh = (long long)B * H;
+  const double tile_s = d == 128 ? 1.35e-6 : 0.40e-6, ovh = d == 128 ? 6.0 : 4.0;
+  const int per_cu = d == 64 ? 2 : 1;
+  std::vector<int> head;   // one head's workgroups, in dispatch order: their key tiles
+  for (int qb = nqb - 1; qb >= 0; --qb) {
+    const int t = ((causal ? std::min(N, (qb + 1) * br) : N) + kBC - 1) / kBC;
+    const int n = r_units > 0 ? (qb + r_units) / r_units : n_splits;
+    for (int sp = n - 1; sp >= 0; --sp)
+      head.push_back((int)((long long)(sp + 1) * t / n - (long long)sp * t / n));
+  }
+  const long long total = bh * (long long)head.size();
+  double span = 0.0;
+  for (int x = 0; x < kXcds; ++x) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+    for (int i = 0; i < 32 * per_cu; ++i) cu.push(0.0);
+    auto place = [&](long long i) {
+      const double t0 = cu.top();
+      cu.pop();
+      cu.push(t0 + (head[(size_t)(i % (long long)head.size())] + ovh) * per_cu);
+    };
+    if (total % kXcds == 0)
+      for (long long i = x * (total / kXcds); i < (x + 1) * (total / kXcds); ++i) place(i);
+    else
+      for (long long i = x; i < total; i += kXcds) place(i);
+    double end = 0.0;
+    while (!cu.empty()) {
+      end = std::max(end, cu.top());
+      cu.pop();
+    }
+    span = std::max(span, end);
+  }
+  const double merge = n_splits > 1 ? 2.0 * n_splits * (double)bh * N * d * 4 / 8e12 + 20e-6 : 0.0;
+  return span * tile_s + merge;
+}
+
+// The range rule fa_fwd_splitkv uses for n_splits: 0 (every query block cut
+// into n_splits ranges) or, under the causal mask, r > 0 (block b cut into
+// ceil((b + 1) / r) ranges, r = ceil(blocks per head / n_splits)), whichever
+// the model above says is faster.
+static int split_rule(int B, int H, int N, int d, int causal, int n_splits) {
+  if (!causal || n_splits <= 1) return 0;
+  const int nqb = (N + rows_per_block(d) - 1) / rows_per_block(d);
+  const int r = (nqb + n_splits - 1) / n_splits;
+  const double t_uniform = split_model_time(B, H, N, d, causal, n_splits, 0);
+  const double t_prop = split_model_time(B, H, N, d, causal, n_splits, r);
+  return t_prop < t_uniform ? r : 0;
+}
+
+extern "C" int fa_fwd_splitkv_ranges(int B, int H, int N, int d, int causal, int n_splits, int* r_units) {
+  long long blocks = 0;
+  const int st = check_shape(B, H, N, d, causal, &blocks);
+  if (st != FA_OK) return st;
+  if (n_splits < 1 || n_splits > kMaxSplits) return FA_ERR_SPLITS;
+  if (r_units) *r_units = split_rule(B, H, N, d, causal, n_splits);
+  return FA_OK;
 }
 
 extern "C" int fa_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int* n_splits,
@@ -969,10 +1074,22 @@ extern "C" int fa_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int* 
   // merge launch), at most 16.  More splits balance the causal block lengths
   // better but cost the fp32 partials' round trip through HBM
   // (2 n_splits B H N d 4 bytes).
+  // the split count (1: fa_fwd alone, no merge) with the smallest modelled
+  // time, each count with its own range rule; ranges of at least 8 key tiles
+  // on the longest block; at most 16
   const long long tiles = ((long long)N + kBC - 1) / kBC;
-  const long long resident = 256LL * (d == 64 ? 2 : 1);
-  long long n = (2 * resident + blocks - 1) / blocks;
-  n = max(1LL, min(n, min(16LL, tiles / 8)));
+  long long n = 1;
+  if (blocks < 2LL * 256 * (d == 64 ? 2 : 1)) {       // fa_fwd alone fills fewer than two rounds
+    double best = split_model_time(B, H, N, d, causal, 1, 0);
+    for (int c = 2; c <= 16 && c <= tiles / 8; ++c) {
+      const int rule = split_rule(B, H, N, d, causal, c);
+      const double t = split_model_time(B, H, N, d, causal, c, rule);
+      if (t < best) {
+        best = t;
+        n = c;
+      }
+    }
+  }
   if (n_splits) *n_splits = (int)n;
   const size_t rows = (size_t)B * H * (size_t)N;
   if (o_part_bytes) *o_part_bytes = (size_t)n * rows * d * 4;
@@ -1017,17 +1134,21 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   __bf16* Op = static_cast<__bf16*>(o);
   __bf16* nb = nullptr;
   float* nl = nullptr;
-  const dim3 grid((unsigned)(blocks * n_splits)), block(threads_per_block(d));
+  // the range rule: n_splits per query block, or under the mask (if the
+  // model prefers it) ceil((b + 1) / r) for query block b, at most n_splits
+  const int r = split_rule(B, H, N, d, causal, n_splits);
+  const long long n_wg = r > 0 ? (long long)BH * causal_units(nqb, r) : blocks * n_splits;
+  const dim3 grid((unsigned)n_wg), block(threads_per_block(d));
   if (d == 128) {
-    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
-    else        hipLaunchKernelGGL((fa_fwd_kernel<128, false, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
+    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<128, true, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, r, c_log2);
+    else        hipLaunchKernelGGL((fa_fwd_kernel<128, false, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, 1, c_log2);
     hipLaunchKernelGGL((fa_merge_kernel<128>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                       o_part, lse_part, Op, lse, (long long)rows, n_splits);
+                       o_part, lse_part, Op, lse, (long long)rows, N, n_splits, r);
   } else {
-    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<64, true, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
-    else        hipLaunchKernelGGL((fa_fwd_kernel<64, false, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, c_log2);
+    if (causal) hipLaunchKernelGGL((fa_fwd_kernel<64, true, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, r, c_log2);
+    else        hipLaunchKernelGGL((fa_fwd_kernel<64, false, true>), grid, block, 0, stream, Q, Kp, Vp, nb, nl, o_part, lse_part, BH, N, nqb, n_splits, 1, c_log2);
     hipLaunchKernelGGL((fa_merge_kernel<64>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream,
-                       o_part, lse_part, Op, lse, (long long)rows, n_splits);
+                       o_part, lse_part, Op, lse, (long long)rows, N, n_splits, r);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

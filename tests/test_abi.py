@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_fa1order", "fa_fwd_fp8", "fa_fwd_fp8_tile",
-                                    "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_fwd_tile", "fa_quant_fp8",
+                                    "fa_fwd_splitkv", "fa_fwd_splitkv_plan", "fa_fwd_splitkv_ranges", "fa_fwd_tile", "fa_quant_fp8",
                                     "fa_status_str"]
 
 
@@ -152,16 +152,32 @@ def test_bad_splitkv_arguments_are_rejected_on_the_host(lib, kw, code):
 
 
 def test_splitkv_plan(lib):
-    # one GPU's share of the 16K causal workload split over 8 GPUs: 4 heads, 256 query blocks
+    # one GPU's share of the 16K causal workload split over 8 GPUs: 4 heads, 256 query blocks, one
+    # round of the CUs with causal lengths from 4 to 256 key tiles: the plan splits it
     n, ob, lb = fa.fa_fwd_splitkv_plan(1, 4, 16384, 128, 1)
-    assert n == 2 and ob == 2 * 4 * 16384 * 128 * 4 and lb == 2 * 4 * 16384 * 4
+    assert 2 <= n <= 16 and ob == n * 4 * 16384 * 128 * 4 and lb == n * 4 * 16384 * 4
     assert fa.fa_fwd_splitkv_plan(1, 32, 16384, 128, 1)[0] == 1      # 2048 blocks fill the GPU
     assert fa.fa_fwd_splitkv_plan(1, 1, 256, 64, 0)[0] == 1          # four 64-key tiles: too short to split
-    assert fa.fa_fwd_splitkv_plan(1, 1, 4096, 64, 0)[0] == 8         # 64 tiles: 8 ranges of 8
-    assert fa.fa_fwd_splitkv_plan(1, 4, 16384, 64, 1)[0] == 2        # 512 blocks, two resident per CU
-    assert fa.fa_fwd_splitkv_plan(1, 2, 16384, 128, 1)[0] == 4       # 128 blocks
+    assert fa.fa_fwd_splitkv_plan(1, 8, 65536, 128, 1)[0] == 1       # 2048 blocks
+    assert 2 <= fa.fa_fwd_splitkv_plan(1, 1, 4096, 64, 0)[0] <= 8     # 64 tiles: ranges of at least 8
+    assert fa.fa_fwd_splitkv_plan(1, 2, 16384, 128, 1)[0] >= 2       # 128 blocks, half the CUs
     with pytest.raises(fa.FaError):
         fa.fa_fwd_splitkv_plan(1, 1, 16, 96, 0)
+
+
+def test_splitkv_range_rule(lib):
+    """Without the mask every block has n_splits ranges; under it the rule is
+    either that or ceil((b + 1) / r) ranges with r = ceil(blocks / n_splits)."""
+    for shp in [(1, 4, 16384, 128), (1, 2, 16384, 128), (1, 8, 8192, 128), (1, 4, 16384, 64), (1, 1, 300, 128)]:
+        br = fa.fa_fwd_tile(*shp, 1)[0]
+        nqb = -(-shp[2] // br)
+        for n in (1, 2, 3, 4, 6, 8):
+            assert fa.fa_fwd_splitkv_ranges(*shp, 0, n) == 0
+            r = fa.fa_fwd_splitkv_ranges(*shp, 1, n)
+            assert r in (0, -(-nqb // n)) and (n > 1 or r == 0)
+    assert fa.fa_fwd_splitkv_ranges(1, 2, 16384, 128, 1, 3) > 0       # measured: proportional is faster here
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_splitkv_ranges(1, 1, 16, 128, 1, 0)
 
 
 # fa_fwd_fa1order: fake addresses; every call is rejected on the host.

@@ -80,13 +80,15 @@ def test_splitkv_is_bitwise_deterministic():
 
 
 @pytest.mark.parametrize("B,H,N,d,causal,n_splits", [(1, 2, 300, 128, True, 5), (1, 2, 300, 64, True, 5),
-                                                     (2, 1, 700, 64, True, 7), (1, 1, 130, 128, False, 4)])
+                                                     (2, 1, 700, 64, True, 7), (1, 1, 130, 128, False, 4),
+                                                     (1, 2, 100, 64, False, 7)])
 def test_partials_of_rows_without_a_visible_key_are_exact_zeros(B, H, N, d, causal, n_splits):
-    """Ranges that start past some rows of a query block leave those rows no
-    visible key: their partials must be exactly O_s = 0 and LSE_s = -inf (they
-    drop out of the two-block merge of the online softmax), and no partial
-    anywhere may hold a NaN (the running statistics of such a row start at
-    -inf and must not form (-inf) - (-inf))."""
+    """A range that holds no key a row may see (more ranges than key tiles)
+    must give that row exactly O_s = 0 and LSE_s = -inf (it drops out of the
+    two-block merge of the online softmax); under the causal mask, ranges a
+    short query block does not have (it gets fewer than n_splits) are neither
+    written nor read; and no partial anywhere may hold a NaN (the running
+    statistics of a row start at -inf and must not form (-inf) - (-inf))."""
     dev = device()
     w = workloads.custom(B, H, N, d, causal, seed=4000 + N + d)
     q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
@@ -98,19 +100,26 @@ def test_partials_of_rows_without_a_visible_key_are_exact_zeros(B, H, N, d, caus
     op, lp = o_part.cpu(), lse_part.cpu()
     assert not torch.isnan(op).any().item() and not torch.isnan(lp).any().item()
     br, kc = fa.fa_fwd_tile(B, H, N, d, int(causal))[:2]
-    n_empty = 0
+    r = fa.fa_fwd_splitkv_ranges(B, H, N, d, int(causal), n_splits)   # > 0: block b has ceil((b + 1) / r)
+    n_empty = n_unused = 0
     for i in range(N):
         q0 = (i // br) * br
         tiles = -(-(min(N, q0 + br) if causal else N) // kc)
+        n_ranges = (i // br + r) // r if r > 0 else n_splits
         for s in range(n_splits):
-            j0, j1 = s * tiles // n_splits, (s + 1) * tiles // n_splits
+            if s >= n_ranges:    # no such range: the workspace is left as it was
+                n_unused += 1
+                assert (op[s, :, :, i] == 7.0).all().item() and (lp[s, :, :, i] == 7.0).all().item()
+                continue
+            j0, j1 = s * tiles // n_ranges, (s + 1) * tiles // n_ranges
             visible = j0 < j1 and (not causal or j0 * kc <= i)
             if visible:
                 assert torch.isfinite(op[s, :, :, i]).all().item() and torch.isfinite(lp[s, :, :, i]).all().item()
             else:
                 n_empty += 1
                 assert (op[s, :, :, i] == 0).all().item() and (lp[s, :, :, i] == -math.inf).all().item()
-    announce(f"[splitkv-empty] {w.name} n_splits={n_splits}: {n_empty} (row, range) pairs with no visible key")
-    assert n_empty > 0
+    announce(f"[splitkv-empty] {w.name} n_splits={n_splits}: {n_empty} (row, range) pairs with no visible key, "
+             f"{n_unused} past the row's ranges")
+    assert n_empty + n_unused > 0
     mo, me, ml = compare_full(*(t.cpu() for t in (q, k, v)), w.scale, causal, o, lse)
     assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS

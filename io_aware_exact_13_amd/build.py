@@ -32,8 +32,8 @@ FLAGS = [
 
 # Variants of the bf16 forward, each overriding compile-time constants of
 # fa_fwd.hip (the default build overrides none).  The tile candidates are for
-# measurement only; "exactmax" and "racecheck" are also built by the default
-# build, because GPU tests compare them with the default library.
+# measurement only; TEST_VARIANTS are also built by the default build, because
+# GPU tests compare them with the default library or the oracle.
 TILE_VARIANTS = {
     "w4d128": ["-DFA_WAVES_D128=4"],       # 4 waves (128 query rows) per workgroup at d = 128
     "w8d64": ["-DFA_WAVES_D64=8"],         # 8 waves (256 query rows) per workgroup at d = 64
@@ -50,8 +50,16 @@ TILE_VARIANTS = {
     "valu4": ["-DFA_VALU_PER_MFMA=4"],     # 4
     "valu5": ["-DFA_VALU_PER_MFMA=5"],     # 5 (all of a d = 128 step's softmax between its MFMAs)
     "racecheck": ["-DFA_EXTRA_BARRIER=1"],  # a wait and a workgroup barrier after every step's LDS reads
+    "g2": ["-DFA_GROUPS_D128=2"],          # d = 128: 4 waves of 64 rows (two row groups), 32-key tiles
+    "g2racecheck": ["-DFA_GROUPS_D128=2", "-DFA_EXTRA_BARRIER=1"],
+    "g2v4": ["-DFA_GROUPS_D128=2", "-DFA_VALU_PER_MFMA=4"],
+    "g2v5": ["-DFA_GROUPS_D128=2", "-DFA_VALU_PER_MFMA=5"],
+    "g2v6": ["-DFA_GROUPS_D128=2", "-DFA_VALU_PER_MFMA=6"],
+    "g2v7": ["-DFA_GROUPS_D128=2", "-DFA_VALU_PER_MFMA=7"],
+    "g2nomax": ["-DFA_GROUPS_D128=2", "-DFA_NOMAX_D128=1"],
+    "nomax128": ["-DFA_NOMAX_D128=1"],
 }
-TEST_VARIANTS = ("exactmax", "racecheck")
+TEST_VARIANTS = ("exactmax", "racecheck", "g2", "g2racecheck")
 
 
 def lib_path(variant: str | None = None) -> str:

@@ -81,7 +81,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kBC = 64;           // keys per K/V tile
 // Tile parameters are compile-time constants.  The defaults are the measured
 // choice; a build may override them to measure another candidate (the
 // library's own build does not).
@@ -99,14 +98,27 @@ constexpr int kBC = 64;           // keys per K/V tile
 #ifndef FA_VALU_PER_MFMA
 #define FA_VALU_PER_MFMA 3
 #endif
-// Waves per workgroup (32 query rows each): 8 at d = 128 (one workgroup per
-// CU, 128 KiB of LDS), 4 at d = 64 (64 KiB, two workgroups per CU, whose
-// waves share the SIMDs and drift apart).
-template <int D> constexpr int kWavesOf = D == 64 ? FA_WAVES_D64 : FA_WAVES_D128;
+// Row groups per wave at d = 128: 1 (32 query rows per wave, 64-key tiles,
+// two waves per SIMD), or 2 (64 rows per wave, 32-key tiles, one wave per
+// SIMD with up to 512 registers a lane): each K or V operand read from LDS
+// then feeds two MFMAs, which halves the LDS operand bytes per FLOP.
+#ifndef FA_GROUPS_D128
+#define FA_GROUPS_D128 1
+#endif
+static_assert(FA_GROUPS_D128 == 1 || FA_GROUPS_D128 == 2, "row groups per wave at d = 128");
+template <int D> constexpr int kGroupsOf = D == 128 ? FA_GROUPS_D128 : 1;
+template <int D> constexpr int kBCOf = kGroupsOf<D> == 2 ? 32 : 64;   // keys per K/V tile
+template <int D> constexpr int kKbOf = kBCOf<D> / 32;                 // 32-key blocks per tile
+template <int D> constexpr int kWavesPerSimdOf = kGroupsOf<D> == 2 ? 1 : 2;
+// Waves per workgroup: 8 at d = 128 (one workgroup per CU, 128 KiB of LDS),
+// 4 at d = 64 (64 KiB, two workgroups per CU, whose waves share the SIMDs
+// and drift apart); 4 at d = 128 with two row groups per wave.
+template <int D> constexpr int kWavesOf = D == 64 ? FA_WAVES_D64 : (FA_GROUPS_D128 == 2 ? 4 : FA_WAVES_D128);
 static_assert(FA_WAVES_D128 == 4 || FA_WAVES_D128 == 8, "waves per workgroup at d = 128");
 static_assert(FA_WAVES_D64 == 4 || FA_WAVES_D64 == 8, "waves per workgroup at d = 64");
 template <int D> constexpr int kThreadsOf = kWavesOf<D> * 64;
-template <int D> constexpr int kBROf = kWavesOf<D> * 32;   // query rows per workgroup
+template <int D> constexpr int kBROf = kWavesOf<D> * 32 * kGroupsOf<D>;   // query rows per workgroup
+__host__ __device__ constexpr int keys_per_tile(int d) { return d == 64 ? kBCOf<64> : kBCOf<128>; }
 __host__ __device__ constexpr int rows_per_block(int d) { return d == 64 ? kBROf<64> : kBROf<128>; }
 __host__ __device__ constexpr int threads_per_block(int d) { return d == 64 ? kThreadsOf<64> : kThreadsOf<128>; }
 constexpr int kXcds = 8;          // accelerator dies; workgroups are dealt to them round-robin
@@ -159,6 +171,10 @@ constexpr float kShare = FA_LAG_SHARE;   // largest share of the row's sum a lag
 #ifndef FA_D64_MAX_TILES
 #define FA_D64_MAX_TILES 8
 #endif
+// d = 128 on the same path as d = 64 (no row maximum past the first tiles)
+#ifndef FA_NOMAX_D128
+#define FA_NOMAX_D128 0
+#endif
 
 // LDS geometry: unpadded rows with XOR-swizzled 16-byte chunks, so a tile is
 // exactly 16 KiB (d=128) and every wave copies the same number of 1 KiB
@@ -172,7 +188,7 @@ template <int D>
 struct Geom {
   static constexpr int kRowBytes = 2 * D;                   // one K or V row
   static constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
-  static constexpr int kTile = kBC * kRowBytes;             // one K or V tile
+  static constexpr int kTile = kBCOf<D> * kRowBytes;        // one K or V tile
   static constexpr int kRing = 4;                           // LDS buffers per operand
   static constexpr int kLdsBytes = 2 * kRing * kTile;
   __host__ __device__ static constexpr int k_buf(int b) { return b * kTile; }            // K buffer b
@@ -203,7 +219,7 @@ struct TileCopy {
     voff = (unsigned)(row * G::kRowBytes + lchunk * 16);
   }
 
-  // Copy key rows [key0, key0 + kBC) of one head into the LDS tile at `dst`.
+  // Copy key rows [key0, key0 + kBCOf<D>) of one head into the LDS tile at `dst`.
   // The buffer runs from row key0 to row N: rows past the end read as zeros,
   // and a tile wholly past the end copies nothing but zeros (no branch).
   __device__ __forceinline__ void issue(const char* head, int key0, int n, char* dst, int wave, int i) const {
@@ -265,23 +281,31 @@ __device__ __forceinline__ float share_slack(float l_row) {
   return fminf(kSlack, fmaxf(0.f, __builtin_amdgcn_logf(l_row) + __builtin_log2f(kShare)));
 }
 
-// S^T = K Q^T for one tile (fp32, unscaled), not overlapped with anything
-// (used once, for S_0).  A operand: K row 32 kb + l32, columns 16 ks + 8 h
-// .. +7; B operand: Q^T from registers.
+// Register sets of one pipeline stage, per row group g of the wave: the S^T
+// accumulators of a tile, P^T as bf16 B operands, and Q^T.
+template <int D> using SSet = f32x16[kGroupsOf<D>][kKbOf<D>];
+template <int D> using PSet = bf16x8[kGroupsOf<D>][kBCOf<D> / 16];
+template <int D> using QSet = bf16x8[kGroupsOf<D>][D / 16];
+
+// S^T = K Q^T for one tile (fp32, unscaled) for each row group, not
+// overlapped with anything (used once, for S_0).  A operand: K row
+// 32 kb + l32, columns 16 ks + 8 h .. +7; B operand: Q^T from registers.
 template <int D>
-__device__ __forceinline__ void scores(const char* Kt, const int (&k_off)[D / 16], const bf16x8 (&qf)[D / 16],
-                                       f32x16 (&s)[kBC / 32]) {
+__device__ __forceinline__ void scores(const char* Kt, const int (&k_off)[D / 16], const QSet<D>& qf, SSet<D>& s) {
   using G = Geom<D>;
 #pragma unroll
-  for (int kb = 0; kb < kBC / 32; ++kb) {
+  for (int kb = 0; kb < kKbOf<D>; ++kb) {
     bf16x8 a[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       a[ks] = *reinterpret_cast<const bf16x8*>(Kt + k_off[ks] + kb * 32 * G::kRowBytes);
-    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
-    for (int ks = 1; ks < D / 16; ++ks)
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], s[kb], 0, 0, 0);
+    for (int g = 0; g < kGroupsOf<D>; ++g) {
+      s[g][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], qf[g][0], f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < D / 16; ++ks)
+        s[g][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[g][ks], s[g][kb], 0, 0, 0);
+    }
   }
 }
 
@@ -310,9 +334,9 @@ __device__ __forceinline__ bf16x8 v_operand(const char* Vt, int v_off_ct, int t)
 // the reference stays, so a slack taken from an earlier, smaller sum is
 // still within the rule.
 template <int D, bool MASKED, bool REFRESH>
-__device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, int lim, int h, float c_log2,
-                                              RowState<D>& st, bf16x8 (&pf)[kBC / 16], bool* rescale) {
-  constexpr int kKb = kBC / 32;
+__device__ __forceinline__ float softmax_tile(f32x16 (&s)[kKbOf<D>], int key0, int lim, int h, float c_log2,
+                                              RowState<D>& st, bf16x8 (&pf)[kBCOf<D> / 16], bool* rescale) {
+  constexpr int kKb = kKbOf<D>;
   if (MASKED) {
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
@@ -374,7 +398,7 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, i
   // compiler sinks the exponentials into the next step, next to the MFMAs
   // that consume them, where they would no longer overlap this step's MFMAs.
 #pragma unroll
-  for (int t = 0; t < kBC / 16; ++t) asm volatile("" : "+v"(pf[t]));
+  for (int t = 0; t < kBCOf<D> / 16; ++t) asm volatile("" : "+v"(pf[t]));
   asm volatile("" : "+v"(st.l_part), "+v"(st.m_ref));
   return alpha;
 }
@@ -382,11 +406,12 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kBC / 32], int key0, i
 // P = exp2(S c + neg_m) for one tile, rounded to bf16 for the MFMA; returns
 // this lane's share of the tile's row sum, taken over the fp32 P (the
 // logsumexp needs the unrounded weights).
-__device__ __forceinline__ float exp_tile(const f32x16 (&s)[kBC / 32], float c_log2, float neg_m,
-                                          bf16x8 (&pf)[kBC / 16]) {
+template <int D>
+__device__ __forceinline__ float exp_tile(const f32x16 (&s)[kKbOf<D>], float c_log2, float neg_m,
+                                          bf16x8 (&pf)[kBCOf<D> / 16]) {
   float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < kBC / 32; ++kb)
+  for (int kb = 0; kb < kKbOf<D>; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, neg_m));
@@ -403,10 +428,11 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[kBC / 32], float c_l
 // catches the first tile, where the reference is -inf and P is inf or NaN).
 // Returns whether some lane of the wave must redo the tile with a new
 // reference (softmax_redo); *lt receives this lane's tile sum.
-template <bool MASKED>
-__device__ __forceinline__ bool softmax_tile_lagged(f32x16 (&s)[kBC / 32], int key0, int lim, int h, float c_log2,
-                                             float m_ref, float l_part, bf16x8 (&pf)[kBC / 16], float* lt) {
-  constexpr int kKb = kBC / 32;
+template <int D, bool MASKED>
+__device__ __forceinline__ bool softmax_tile_lagged(f32x16 (&s)[kKbOf<D>], int key0, int lim, int h, float c_log2,
+                                                    float m_ref, float l_part, bf16x8 (&pf)[kBCOf<D> / 16],
+                                                    float* lt) {
+  constexpr int kKb = kKbOf<D>;
   if (MASKED) {
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
@@ -416,12 +442,12 @@ __device__ __forceinline__ bool softmax_tile_lagged(f32x16 (&s)[kBC / 32], int k
         if (key > lim) s[kb][r] = -INFINITY;
       }
   }
-  float sum = exp_tile(s, c_log2, -m_ref, pf);
+  float sum = exp_tile<D>(s, c_log2, -m_ref, pf);
   // Materialise P and the sum here: without these empty asm uses the
   // compiler sinks the exponentials into the next step, next to the MFMAs
   // that consume them, where they would no longer overlap this step's MFMAs.
 #pragma unroll
-  for (int t = 0; t < kBC / 16; ++t) asm volatile("" : "+v"(pf[t]));
+  for (int t = 0; t < kBCOf<D> / 16; ++t) asm volatile("" : "+v"(pf[t]));
   asm volatile("" : "+v"(sum));
   *lt = sum;
   // accepted: every P of the lane is <= its tile sum, which is <= 1 (no
@@ -437,9 +463,9 @@ __device__ __forceinline__ bool softmax_tile_lagged(f32x16 (&s)[kBC / 32], int k
 // alpha = exp2(m_old - m_new), the factor for the running sum and the
 // accumulators (0 on the first tile, 1 where the reference stays).
 template <int D>
-__device__ __forceinline__ float softmax_redo(const f32x16 (&s)[kBC / 32], float c_log2, RowState<D>& st,
-                                              bf16x8 (&pf)[kBC / 16], float* lt) {
-  constexpr int kKb = kBC / 32;
+__device__ __forceinline__ float softmax_redo(const f32x16 (&s)[kKbOf<D>], float c_log2, RowState<D>& st,
+                                              bf16x8 (&pf)[kBCOf<D> / 16], float* lt) {
+  constexpr int kKb = kKbOf<D>;
   // row max: a three-way tree over this lane's 16 kKb scores, then the other
   // half's.  The IEEE maximum (NaN-propagating) maps to v_maximum3_f32 and,
   // unlike fmaxf, needs no canonicalising moves of the MFMA results.
@@ -466,7 +492,7 @@ __device__ __forceinline__ float softmax_redo(const f32x16 (&s)[kBC / 32], float
   const float m_new = fmaxf(st.m_ref, m_tile);
   const float alpha = (m_new == st.m_ref) ? 1.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
   st.m_ref = m_new;
-  *lt = exp_tile(s, c_log2, (m_new == -INFINITY) ? 0.f : -m_new, pf);
+  *lt = exp_tile<D>(s, c_log2, (m_new == -INFINITY) ? 0.f : -m_new, pf);
   return alpha;
 }
 
@@ -476,7 +502,8 @@ struct Ctx {
   const char* Kh;
   const char* Vh;
   char* lds;
-  int N, kv_end, n_tiles, lim, wave, h;
+  int N, kv_end, n_tiles, wave, h;
+  int lim[kGroupsOf<D>];   // last key each of the lane's rows (one per row group) may see
   float c_log2;
   int k_off[D / 16];    // lane's LDS offset of its K operand for k-step ks (32-row block 0)
   int v_off[D / 32];    // lane's LDS offset of its first transposed V read for column tile ct
@@ -501,15 +528,15 @@ struct Ctx {
 template <int D, bool MASKED, bool NOMAX, bool REFRESH>
 __device__ __forceinline__ void step(const char* __restrict__ k_read, const char* __restrict__ v_read,
                                      char* __restrict__ k_fill, char* __restrict__ v_fill, const Ctx<D>& c,
-                                     int j, const bf16x8 (&qf)[D / 16], f32x16 (&s_in)[kBC / 32],
-                                     f32x16 (&s_out)[kBC / 32], const bf16x8 (&p_in)[kBC / 16],
-                                     bf16x8 (&p_out)[kBC / 16], RowState<D>& st) {
+                                     int j, const QSet<D>& qf, SSet<D>& s_in, SSet<D>& s_out, const PSet<D>& p_in,
+                                     PSet<D>& p_out, RowState<D> (&st)[kGroupsOf<D>]) {
   using G = Geom<D>;
-  constexpr int kCt = D / 32, kKs = kBC / 16, kKb = kBC / 32, kDs = D / 16;
-  constexpr int kPV = kKs * kCt;        // P V steps: (t, ct), ct fastest
-  constexpr int kS = kDs * kKb;         // S steps: (ks, kb), kb fastest
-  static_assert(kPV == kS, "P V and S step counts are interleaved one to one");
-  constexpr int kAhead = FA_OPERAND_AHEAD;   // step pairs whose operands are requested ahead
+  constexpr int kG = kGroupsOf<D>, kBC = kBCOf<D>;
+  constexpr int kCt = D / 32, kKs = kBC / 16, kKb = kKbOf<D>, kDs = D / 16;
+  constexpr int kPV = kKs * kCt;        // P V operand reads: (t, ct), ct fastest
+  constexpr int kS = kDs * kKb;         // S operand reads: (ks, kb), kb fastest
+  static_assert(kPV == kS, "P V and S operand reads are interleaved one to one");
+  constexpr int kAhead = FA_OPERAND_AHEAD;   // operand pairs requested ahead
 
   // this wave's copies of K_{j+1}, V_{j-1} (issued two steps ago; the
   // previous step's copies may still be in flight) ...
@@ -518,17 +545,23 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   __builtin_amdgcn_sched_barrier(0);
 
   bf16x8 v_op[kPV], k_op[kS];
-  auto fetch = [&](int i) {             // operands of P V step i and S step i
+  auto fetch = [&](int i) {             // operands of P V read i and S read i
     const int t = i / kCt, ct = i % kCt;
     v_op[i] = v_operand<D>(v_read, c.v_off[ct], t);
     const int ks = i / kKb, kb = i % kKb;
     k_op[i] = *reinterpret_cast<const bf16x8*>(k_read + c.k_off[ks] + kb * 32 * G::kRowBytes);
   };
+  // each operand feeds one MFMA per row group
   auto mfma = [&](int i) {
     const int t = i / kCt, ct = i % kCt;
-    st.acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_op[i], p_in[t], st.acc[ct], 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < kG; ++g)
+      st[g].acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_op[i], p_in[g][t], st[g].acc[ct], 0, 0, 0);
     const int ks = i / kKb, kb = i % kKb;
-    s_out[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_op[i], qf[ks], ks == 0 ? f32x16{} : s_out[kb], 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < kG; ++g)
+      s_out[g][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_op[i], qf[g][ks], ks == 0 ? f32x16{} : s_out[g][kb],
+                                                             0, 0, 0);
   };
   // The copies go out between the MFMAs: a copy instruction holds up its
   // wave for tens of cycles at issue, which the MFMAs already in the pipe
@@ -552,23 +585,33 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   // maximum (about 5% faster there; no gain for d = 128, whose MFMA work per
   // tile hides the max tree)
   constexpr bool kNoMax = NOMAX && !FA_EXACT_MAX;
-  bool rescale = false;
-  float alpha = 1.f, lt = 0.f;
-  if constexpr (kNoMax)
-    rescale = softmax_tile_lagged<MASKED>(s_in, j * kBC, c.lim, c.h, c.c_log2, st.m_ref, st.l_part, p_out, &lt);
-  else alpha = softmax_tile<D, MASKED, REFRESH>(s_in, j * kBC, c.lim, c.h, c.c_log2, st, p_out, &rescale);
-  // Interleave: each step pair is two MFMAs, its operand reads and an equal
-  // share of the softmax's VALU work between and after them (mask 0x008
-  // MFMA, 0x100 LDS read, 0x002 VALU, 0x010 VMEM).
+  bool rescale[kG];
+  float alpha[kG], lt[kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    rescale[g] = false;
+    alpha[g] = 1.f;
+    lt[g] = 0.f;
+    if constexpr (kNoMax)
+      rescale[g] = softmax_tile_lagged<D, MASKED>(s_in[g], j * kBC, c.lim[g], c.h, c.c_log2, st[g].m_ref,
+                                                  st[g].l_part, p_out[g], &lt[g]);
+    else
+      alpha[g] = softmax_tile<D, MASKED, REFRESH>(s_in[g], j * kBC, c.lim[g], c.h, c.c_log2, st[g], p_out[g],
+                                                  &rescale[g]);
+  }
+  // Interleave: each operand pair is 2 kG MFMAs, its operand reads and an
+  // equal share of the softmax's VALU work between and after them (mask
+  // 0x008 MFMA, 0x100 LDS read, 0x002 VALU, 0x010 VMEM).
   __builtin_amdgcn_sched_group_barrier(0x100, 3 * kAhead, 0);
 #pragma unroll
   for (int i = 0; i < kPV; ++i) {
     if (i + kAhead < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, FA_VALU_PER_MFMA, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i % kCopyEvery == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, FA_VALU_PER_MFMA, 0);
+#pragma unroll
+    for (int m = 0; m < 2 * kG; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m == 2 * kG - 1 && i % kCopyEvery == 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, FA_VALU_PER_MFMA, 0);
+    }
   }
   if constexpr (FA_EXTRA_BARRIER) {
     __builtin_amdgcn_sched_barrier(0);
@@ -576,21 +619,24 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (kNoMax) {
-    if (rescale) {
-      alpha = softmax_redo<D>(s_in, c.c_log2, st, p_out, &lt);
-      st.l_part *= alpha;
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    if constexpr (kNoMax) {
+      if (rescale[g]) {
+        alpha[g] = softmax_redo<D>(s_in[g], c.c_log2, st[g], p_out[g], &lt[g]);
+        st[g].l_part *= alpha[g];
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[g].acc[ct][r] *= alpha[g];
+      }
+      st[g].l_part += lt[g];
+    } else if (rescale[g]) {
 #pragma unroll
       for (int ct = 0; ct < kCt; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st.acc[ct][r] *= alpha;
+        for (int r = 0; r < 16; ++r) st[g].acc[ct][r] *= alpha[g];
     }
-    st.l_part += lt;
-  } else if (rescale) {
-#pragma unroll
-    for (int ct = 0; ct < kCt; ++ct)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[ct][r] *= alpha;
   }
 }
 
@@ -599,9 +645,8 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
 // buffer (j-1)%4, and fills K buffer (j+3)%4 and V buffer (j+1)%4.
 // The share rule's slack is refreshed at the first step of every four.
 template <int D, bool MASKED, int PH, bool NOMAX = false>
-__device__ __forceinline__ void step_at(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
-                                        f32x16 (&sa)[kBC / 32], f32x16 (&sb)[kBC / 32],
-                                        bf16x8 (&pa)[kBC / 16], bf16x8 (&pb)[kBC / 16], RowState<D>& st) {
+__device__ __forceinline__ void step_at(const Ctx<D>& c, int j, const QSet<D>& qf, SSet<D>& sa, SSet<D>& sb,
+                                        PSet<D>& pa, PSet<D>& pb, RowState<D> (&st)[kGroupsOf<D>]) {
   using G = Geom<D>;
   constexpr int R = G::kRing;
   if constexpr (PH % 2 == 0)
@@ -615,9 +660,8 @@ __device__ __forceinline__ void step_at(const Ctx<D>& c, int j, const bf16x8 (&q
 }
 
 template <int D, bool MASKED, bool NOMAX = false>
-__device__ __forceinline__ void step_quad(const Ctx<D>& c, int j, const bf16x8 (&qf)[D / 16],
-                                          f32x16 (&sa)[kBC / 32], f32x16 (&sb)[kBC / 32],
-                                          bf16x8 (&pa)[kBC / 16], bf16x8 (&pb)[kBC / 16], RowState<D>& st) {
+__device__ __forceinline__ void step_quad(const Ctx<D>& c, int j, const QSet<D>& qf, SSet<D>& sa, SSet<D>& sb,
+                                          PSet<D>& pa, PSet<D>& pb, RowState<D> (&st)[kGroupsOf<D>]) {
   step_at<D, MASKED, 0, NOMAX>(c, j, qf, sa, sb, pa, pb, st);
   step_at<D, MASKED, 1, NOMAX>(c, j + 1, qf, sa, sb, pa, pb, st);
   step_at<D, MASKED, 2, NOMAX>(c, j + 2, qf, sa, sb, pa, pb, st);
@@ -632,7 +676,7 @@ __device__ __forceinline__ void step_quad(const Ctx<D>& c, int j, const bf16x8 (
 // (causal_units), the longest blocks' ranges first.  Otherwise the workgroup
 // covers all the tiles and writes O (bf16) and LSE.
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreadsOf<D>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimdOf<D>, kWavesPerSimdOf<D>)))
 void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                    const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                    float* __restrict__ Opart, float* __restrict__ Lpart,
@@ -640,6 +684,8 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   using G = Geom<D>;
   constexpr int kDs = D / 16;
   constexpr int kCt = D / 32;
+  constexpr int kG = kGroupsOf<D>;
+  constexpr int kBC = kBCOf<D>;
 
   __shared__ __attribute__((aligned(1024))) char lds[G::kLdsBytes];
 
@@ -648,7 +694,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const int lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   c.h = lane >> 5;                  // which half of the 64 lanes
-  const int l32 = lane & 31;        // this lane's query row within the wave
+  const int l32 = lane & 31;        // this lane's query row within each 32-row group
 
   // ---- workgroup -> (head, query block).  Workgroups are dealt round-robin
   // to the 8 XCDs; the logical index gives each XCD a contiguous run of whole
@@ -681,9 +727,14 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
   constexpr int kBR = kBROf<D>;
   const int q0 = qb * kBR;
-  const int qrow = q0 + c.wave * 32 + l32;   // this lane's query
+  // this lane's queries: row l32 of each of the wave's 32-row groups
+  int qrow[kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    qrow[g] = q0 + (c.wave * kG + g) * 32 + l32;
+    c.lim[g] = CAUSAL ? min(qrow[g], N - 1) : N - 1;   // last key the row may see
+  }
   c.N = N;
-  c.lim = CAUSAL ? min(qrow, N - 1) : N - 1;   // last key this lane may see
   c.c_log2 = c_log2;
   c.lds = lds;
 
@@ -705,12 +756,14 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   j_mask = min(j_mask, c.n_tiles);
   const size_t prow = ((size_t)split * BH + bh) * (size_t)N;   // partial row base (SPLIT)
   if (SPLIT && j0 == c.n_tiles) {                       // an empty share: O_s = 0, LSE_s = -inf
-    if (qrow < N) {
-      float* op = Opart + (prow + qrow) * D;
 #pragma unroll
-      for (int t = 0; t < D / 8; ++t) *reinterpret_cast<f32x4*>(op + 8 * t + 4 * c.h) = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (c.h == 0) Lpart[prow + qrow] = -INFINITY;
-    }
+    for (int g = 0; g < kG; ++g)
+      if (qrow[g] < N) {
+        float* op = Opart + (prow + qrow[g]) * D;
+#pragma unroll
+        for (int t = 0; t < D / 8; ++t) *reinterpret_cast<f32x4*>(op + 8 * t + 4 * c.h) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (c.h == 0) Lpart[prow + qrow[g]] = -INFINITY;
+      }
     return;
   }
 
@@ -744,29 +797,33 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int i = tid; i < G::kTile / 8; i += kThreadsOf<D>)   // V_{-1} = 0
     reinterpret_cast<u32x2*>(lds + G::v_buf(G::kRing - 1))[i] = u32x2{0u, 0u};
 
-  // Q^T operand: lane holds Q[qrow][16*ks + 8*h .. +7] for each k-step
-  bf16x8 qf[kDs];
-  {
-    const bool ok = qrow < N;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + head_off + (size_t)(ok ? qrow : 0) * D);
+  // Q^T operand: lane holds Q[qrow[g]][16*ks + 8*h .. +7] for each k-step
+  QSet<D> qf;
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const bool ok = qrow[g] < N;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + head_off + (size_t)(ok ? qrow[g] : 0) * D);
 #pragma unroll
     for (int ks = 0; ks < kDs; ++ks) {
       bf16x8 x = src[ks * 2 + c.h];
       if (!ok) x = bf16x8{};
-      qf[ks] = x;
+      qf[g][ks] = x;
     }
   }
 
-  RowState<D> st;
+  RowState<D> st[kG];
+  SSet<D> sa, sb;
+  PSet<D> pa, pb;
 #pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) st.acc[ct] = f32x16{};
-  st.m_ref = -INFINITY;
-  st.l_part = 0.f;
-  st.slack = 0.f;
-  f32x16 sa[kBC / 32], sb[kBC / 32];
-  bf16x8 pa[kBC / 16], pb[kBC / 16];
+  for (int g = 0; g < kG; ++g) {
 #pragma unroll
-  for (int t = 0; t < kBC / 16; ++t) pa[t] = bf16x8{};
+    for (int ct = 0; ct < kCt; ++ct) st[g].acc[ct] = f32x16{};
+    st[g].m_ref = -INFINITY;
+    st[g].l_part = 0.f;
+    st[g].slack = 0.f;
+#pragma unroll
+    for (int t = 0; t < kBC / 16; ++t) pa[g][t] = bf16x8{};
+  }
 
   wait_vmcnt<2 * G::kLoads>();                          // K_0, K_1
   __syncthreads();
@@ -777,7 +834,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   int j = j0;
   const int j_fast = max(j0, j_mask);                   // tiles [j0, j_fast) need no mask
   // d = 64: the row maximum on the first FA_D64_MAX_TILES tiles, none after
-  constexpr bool kNoMax = D == 64;
+  constexpr bool kNoMax = D == 64 || FA_NOMAX_D128;
   if constexpr (kNoMax) {
     const int j_max = min(j_fast, j0 + FA_D64_MAX_TILES);
     for (; j + 4 <= j_max; j += 4) step_quad<D, false, false>(c, j, qf, sa, sb, pa, pb, st);
@@ -793,73 +850,86 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   {
     const int last = c.n_tiles - 1 - j0;
     const char* vt = lds + G::v_rel(last % G::kRing);
-    const bf16x8 (&pl)[kBC / 16] = ((last + 1) & 1) ? pb : pa;
+    const PSet<D>& pl = ((last + 1) & 1) ? pb : pa;
 #pragma unroll
     for (int t = 0; t < kBC / 16; ++t)
 #pragma unroll
-      for (int ct = 0; ct < kCt; ++ct)
-        st.acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(vt, c.v_off[ct], t), pl[t],
-                                                             st.acc[ct], 0, 0, 0);
+      for (int ct = 0; ct < kCt; ++ct) {
+        const bf16x8 vop = v_operand<D>(vt, c.v_off[ct], t);
+#pragma unroll
+        for (int g = 0; g < kG; ++g)
+          st[g].acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pl[g][t], st[g].acc[ct], 0, 0, 0);
+      }
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m_ref + log2 l) * ln 2
-  const float l_tot = sum_halves(st.l_part);
+  float l_tot[kG];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) l_tot[g] = sum_halves(st[g].l_part);
   if (SPLIT) {
     // fp32 partial; a row with no visible key in this share has l = 0
-    if (qrow < N) {
-      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-      float* op = Opart + (prow + qrow) * D;
 #pragma unroll
-      for (int ct = 0; ct < kCt; ++ct)
+    for (int g = 0; g < kG; ++g)
+      if (qrow[g] < N) {
+        const float inv = l_tot[g] > 0.f ? 1.0f / l_tot[g] : 0.f;
+        float* op = Opart + (prow + qrow[g]) * D;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<f32x4*>(op + ct * 32 + r4 * 8 + c.h * 4) =
-              f32x4{st.acc[ct][r4 * 4] * inv, st.acc[ct][r4 * 4 + 1] * inv, st.acc[ct][r4 * 4 + 2] * inv,
-                    st.acc[ct][r4 * 4 + 3] * inv};
-      if (c.h == 0) Lpart[prow + qrow] = l_tot > 0.f ? (st.m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-    }
+        for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<f32x4*>(op + ct * 32 + r4 * 8 + c.h * 4) =
+                f32x4{st[g].acc[ct][r4 * 4] * inv, st[g].acc[ct][r4 * 4 + 1] * inv,
+                      st[g].acc[ct][r4 * 4 + 2] * inv, st[g].acc[ct][r4 * 4 + 3] * inv};
+        if (c.h == 0)
+          Lpart[prow + qrow[g]] = l_tot[g] > 0.f ? (st[g].m_ref + log2f(l_tot[g])) * kLn2 : -INFINITY;
+      }
     return;
   }
-  // O = acc / l in bf16, staged through this wave's 32-row slice of the K
-  // ring (idle since the barrier above: every K read and copy has finished)
-  // so that the stores to HBM are whole rows, 16 bytes a lane: a lane's own
-  // accumulators hold 8-byte pieces of one row, which stored directly touch
-  // 32 rows per instruction.  Chunk ch of staged row r sits at 16-byte slot
-  // ch ^ (r % kChunks) of the row, so the 32 rows written by one instruction
-  // spread over the banks.
+  // O = acc / l in bf16, staged group by group through this wave's 32-row
+  // slice of the K ring (idle since the barrier above: every K read and copy
+  // has finished) so that the stores to HBM are whole rows, 16 bytes a lane:
+  // a lane's own accumulators hold 8-byte pieces of one row, which stored
+  // directly touch 32 rows per instruction.  Chunk ch of staged row r sits at
+  // 16-byte slot ch ^ (r % kChunks) of the row, so the 32 rows written by one
+  // instruction spread over the banks.
   {
     constexpr int kChunks = G::kChunks;
     static_assert(kWavesOf<D> * 32 * G::kRowBytes <= G::kRing * G::kTile, "staging fits the K ring");
     char* stage = lds + G::k_buf(0) + c.wave * 32 * G::kRowBytes;
-    const float inv = qrow < N ? 1.0f / l_tot : 0.f;
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct)
+    for (int g = 0; g < kG; ++g) {
+      // the previous group's read-back has returned before its slots are rewritten
+      if (g > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const float inv = qrow[g] < N ? 1.0f / l_tot[g] : 0.f;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const __bf16 b0 = (__bf16)(st.acc[ct][r4 * 4 + 0] * inv);
-        const __bf16 b1 = (__bf16)(st.acc[ct][r4 * 4 + 1] * inv);
-        const __bf16 b2 = (__bf16)(st.acc[ct][r4 * 4 + 2] * inv);
-        const __bf16 b3 = (__bf16)(st.acc[ct][r4 * 4 + 3] * inv);
-        u32x2 w;
-        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        // columns ct*32 + r4*8 + 4h .. +3: chunk 4ct + r4, half h
-        const int ch = ct * 4 + r4;
-        *reinterpret_cast<u32x2*>(stage + l32 * G::kRowBytes + ((ch ^ (l32 % kChunks)) << 4) + 8 * c.h) = w;
+      for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const __bf16 b0 = (__bf16)(st[g].acc[ct][r4 * 4 + 0] * inv);
+          const __bf16 b1 = (__bf16)(st[g].acc[ct][r4 * 4 + 1] * inv);
+          const __bf16 b2 = (__bf16)(st[g].acc[ct][r4 * 4 + 2] * inv);
+          const __bf16 b3 = (__bf16)(st[g].acc[ct][r4 * 4 + 3] * inv);
+          u32x2 w;
+          w[0] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+          w[1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+          // columns ct*32 + r4*8 + 4h .. +3: chunk 4ct + r4, half h
+          const int ch = ct * 4 + r4;
+          *reinterpret_cast<u32x2*>(stage + l32 * G::kRowBytes + ((ch ^ (l32 % kChunks)) << 4) + 8 * c.h) = w;
+        }
+      // the wave reads back what its other lanes wrote: wait for the writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int row0 = q0 + (c.wave * kG + g) * 32;
+#pragma unroll
+      for (int i = 0; i < kChunks / 2; ++i) {
+        const int q = i * 64 + lane, r = q / kChunks, ch = q % kChunks;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * G::kRowBytes + ((ch ^ (r % kChunks)) << 4));
+        if (row0 + r < N) *reinterpret_cast<u32x4*>(O + head_off + (size_t)(row0 + r) * D + ch * 8) = val;
       }
-    // the wave reads back what its other lanes wrote: wait for the writes
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int row0 = q0 + c.wave * 32;
-#pragma unroll
-    for (int i = 0; i < kChunks / 2; ++i) {
-      const int q = i * 64 + lane, r = q / kChunks, ch = q % kChunks;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * G::kRowBytes + ((ch ^ (r % kChunks)) << 4));
-      if (row0 + r < N) *reinterpret_cast<u32x4*>(O + head_off + (size_t)(row0 + r) * D + ch * 8) = val;
     }
   }
-  if (qrow < N) {
-    if (c.h == 0) LSE[(size_t)bh * N + qrow] = (st.m_ref + log2f(l_tot)) * kLn2;
-  }
+#pragma unroll
+  for (int g = 0; g < kG; ++g)
+    if (qrow[g] < N && c.h == 0) LSE[(size_t)bh * N + qrow[g]] = (st[g].m_ref + log2f(l_tot[g])) * kLn2;
 }
 
 // Merge of n_splits partial results of the same rows over disjoint key
@@ -952,7 +1022,7 @@ extern "C" int fa_fwd_tile(int B, int H, int N, int d, int causal, int* rows_per
   const int st = check_shape(B, H, N, d, causal, &g);
   if (st != FA_OK) return st;
   if (rows_per_block) *rows_per_block = ::rows_per_block(d);
-  if (keys_per_tile) *keys_per_tile = kBC;
+  if (keys_per_tile) *keys_per_tile = ::keys_per_tile(d);
   if (waves) *waves = threads_per_block(d) / 64;
   if (blocks) *blocks = g;
   return FA_OK;
@@ -1003,6 +1073,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
 // shares of 2 to 8 heads of 8K-16K tokens): per 64-key tile 1.35 us at
 // d = 128 and 0.40 us at d = 64 (two workgroups per CU, each at half speed),
 // 6 and 4 tiles of overhead per workgroup, and the merge at 8 TB/s plus 20 us.
+constexpr int kModelKeys = 64;   // the model's unit of work: a 64-key tile, whatever the kernel's own tile
 static double split_model_time(int B, int H, int N, int d, int causal, int n_splits, int r_units) {
   const int br = rows_per_block(d);
   const int nqb = (N + br - 1) / br;
@@ -1011,7 +1082,7 @@ static double split_model_time(int B, int H, int N, int d, int causal, int n_spl
   const int per_cu = d == 64 ? 2 : 1;
   std::vector<int> head;   // one head's workgroups, in dispatch order: their key tiles
   for (int qb = nqb - 1; qb >= 0; --qb) {
-    const int t = ((causal ? std::min(N, (qb + 1) * br) : N) + kBC - 1) / kBC;
+    const int t = ((causal ? std::min(N, (qb + 1) * br) : N) + kModelKeys - 1) / kModelKeys;
     const int n = r_units > 0 ? (qb + r_units) / r_units : n_splits;
     for (int sp = n - 1; sp >= 0; --sp)
       head.push_back((int)((long long)(sp + 1) * t / n - (long long)sp * t / n));
@@ -1077,7 +1148,7 @@ extern "C" int fa_fwd_splitkv_plan(int B, int H, int N, int d, int causal, int* 
   // the split count (1: fa_fwd alone, no merge) with the smallest modelled
   // time, each count with its own range rule; ranges of at least 8 key tiles
   // on the longest block; at most 16
-  const long long tiles = ((long long)N + kBC - 1) / kBC;
+  const long long tiles = ((long long)N + kModelKeys - 1) / kModelKeys;
   long long n = 1;
   if (blocks < 2LL * 256 * (d == 64 ? 2 : 1)) {       // fa_fwd alone fills fewer than two rounds
     double best = split_model_time(B, H, N, d, causal, 1, 0);

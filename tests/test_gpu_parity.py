@@ -293,6 +293,25 @@ def test_extra_barrier_build_is_bitwise_equal(B, H, N, d, causal, workload):
     assert torch.equal(lse.view(torch.int32), l2.view(torch.int32))
 
 
+@pytest.mark.parametrize("B,H,N,causal", [(1, 1, 65, False), (2, 3, 513, True), (1, 2, 1000, True),
+                                           (2, 2, 2048, False)])
+def test_row_group_build_matches_oracle(B, H, N, causal):
+    """The d = 128 build with two 32-row groups per wave and 32-key tiles
+    (one wave per SIMD) against the oracle on every element, and bit for bit
+    against its own extra-barrier build (no race on its LDS rings)."""
+    dev = device()
+    w = workloads.custom(B, H, N, 128, causal, seed=1300 + N + int(causal))
+    q, k, v = workloads.make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = variant_fwd("g2", qd, kd, vd, w.scale, causal)
+    o2, l2 = variant_fwd("g2racecheck", qd, kd, vd, w.scale, causal)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), l2.view(torch.int32))
+    mo, me, ml = compare_full(q, k, v, w.scale, causal, o, lse)
+    announce(f"[row groups] {w.name}: max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_exact_running_max_build_keeps_a_late_dominant_key_exact(d):
     """The build whose reference maximum is the running row maximum itself

@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "cdna4.h"
 #include "fa.h"
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const __bf16* __restr
 //   P    = exp2(S^T c - LSE log2 e),  dS = P (dP - D)   (masked keys give 0)
 //   dQ^T += K^T dS^T                      (A: K^T by transposed reads; B: dS from registers)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWavesPerSimd<D>))) void fa_bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void fa_bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dQ, int BH, int N, int n_qblocks, float c_log2, float scale) {
@@ -174,8 +175,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWa
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) acc[ct] = f32x16{};
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
+  // One key tile.  MASKED: the tile holds a key past N or past some row's
+  // diagonal; other tiles skip the visibility test.  `buf` (the tile's
+  // double buffer) is a compile-time constant, so the LDS addresses are the
+  // lanes' offsets plus immediates.
+  auto tile = [&](auto masked, auto buf, int j) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of tile j
     __syncthreads();                                   // everyone's; tile j-1 no longer read
     if (j + 1 < n_tiles) {
@@ -199,14 +204,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWa
         dp[kb] = mfma32(row_operand<D>(Vt, 32 * kb, ks, lane), dof[ks], dp[kb]);
       }
 
-    // register r of block kb: key j 64 + 32 kb + (r / 4) 8 + 4 h + r % 4
+    // register r of block kb: key j 64 + 4 h + (32 kb + (r / 4) 8 + r % 4),
+    // visible (masked tiles) when that is <= lim
+    const int room = lim - j * kKTile - 4 * h;
     bf16x8 dsf[kKTile / 16];
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j * kKTile + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        const float p = key <= lim ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, neg_lse2)) : 0.f;
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, neg_lse2));
+        const float p = (!kMasked || room >= kb * 32 + (r >> 2) * 8 + (r & 3)) ? pe : 0.f;
         dsf[kb * 2 + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dlt));
       }
 
@@ -214,6 +221,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWa
     for (int t = 0; t < kKTile / 16; ++t)
 #pragma unroll
       for (int ct = 0; ct < kCt; ++ct) acc[ct] = mfma32(tr_operand<D>(Kt, 16 * t, ct, lane), dsf[t], acc[ct]);
+  };
+  // Tiles [0, j_hi) hold keys visible to every row of the block (at most
+  // its first row and below N); they go unmasked in pairs, the first of
+  // each in buffer 0, and the rest masked in pairs.
+  const int j_hi = min(CAUSAL ? (q0 + 1) / kKTile : N / kKTile, N / kKTile) & ~1;
+  int j = 0;
+  for (; j < j_hi; j += 2) {
+    tile(std::false_type{}, std::integral_constant<int, 0>{}, j);
+    tile(std::false_type{}, std::integral_constant<int, 1>{}, j + 1);
+  }
+  for (; j < n_tiles; j += 2) {
+    tile(std::true_type{}, std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_tiles) tile(std::true_type{}, std::integral_constant<int, 1>{}, j + 1);
   }
 
   if (qok) {
@@ -231,7 +251,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWa
 //   P  = exp2(S c - LSE log2 e),  dS = P (dP - D)      (rows past N or above the key give 0)
 //   dV^T += dO^T P,  dK^T += Q^T dS       (A: dO^T, Q^T by transposed reads; B: P, dS)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWavesPerSimd<D>))) void fa_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int N, int n_kblocks, float c_log2,
@@ -291,8 +311,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWa
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) { acc_dk[ct] = f32x16{}; acc_dv[ct] = f32x16{}; }
 
-  for (int i = t0; i < n_qt; ++i) {
-    const int buf = (i - t0) & 1;
+  // One query tile.  MASKED: the tile holds a query row past N or a (key,
+  // query) pair above the diagonal for some wave of the workgroup; other
+  // tiles skip the visibility test.  `buf` is the tile's double buffer, a
+  // compile-time constant on the unmasked tiles (their LDS addresses are
+  // then the lanes' offsets plus immediates).
+  auto tile = [&](auto masked, auto buf, int i) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of tile i
     __syncthreads();                                   // everyone's; tile i-1 no longer read
     if (i + 1 < n_qt) issue_tile(i + 1, lds + (buf ^ 1) * kBufBytes);
@@ -310,6 +335,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWa
     // register r: query i 32 + (r / 4) 8 + 4 h + r % 4; its LSE and D sit
     // four at a time in the statistics tile
     bf16x8 pf[2], dsf[2];
+    // masked tiles: register r holds query q = i 32 + 4 h + (8 m + e); it is
+    // visible when q - key = dq + 8 m + e >= 0 and 8 m + e < N - (i 32 + 4 h)
+    const int dq = i * kQTile + 4 * h - key, rem = N - i * kQTile - 4 * h;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const f32x4 lse4 = *reinterpret_cast<const f32x4*>(St + (8 * m + 4 * h) * 4);
@@ -317,9 +345,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWa
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * m + e;
-        const int q = i * kQTile + 8 * m + 4 * h + e;
-        const bool vis = q < N && (!CAUSAL || key <= q);
-        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -lse4[e] * kLog2e)) : 0.f;
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -lse4[e] * kLog2e));
+        float p = pe;
+        if constexpr (kMasked) p = (8 * m + e < rem && (!CAUSAL || dq >= -(8 * m + e))) ? pe : 0.f;
         pf[r >> 3][r & 7] = (__bf16)p;
         dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[e]));
       }
@@ -332,7 +360,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, kWa
         acc_dv[ct] = mfma32(tr_operand<D>(dOt, 16 * t, ct, lane), pf[t], acc_dv[ct]);
         acc_dk[ct] = mfma32(tr_operand<D>(Qt, 16 * t, ct, lane), dsf[t], acc_dk[ct]);
       }
+  };
+  // Every (key, query) pair of tile i is visible to the whole workgroup
+  // when its first query is at or past the block's last key and its last
+  // query is below N.  Tiles go in pairs, the first of each in buffer 0:
+  // masked pairs up to i_lo, unmasked pairs up to i_hi, masked pairs after.
+  const int i_lo = min(n_qt, t0 + ((max(t0, CAUSAL ? (k0 + kKBlock - 1 + kQTile - 1) / kQTile : t0) - t0 + 1) & ~1));
+  const int i_hi = i_lo + ((max(i_lo, min(n_qt, N / kQTile)) - i_lo) & ~1);
+  auto masked_pairs = [&](int& i, int end) __attribute__((always_inline)) {
+    for (; i < end; i += 2) {
+      tile(std::true_type{}, std::integral_constant<int, 0>{}, i);
+      if (i + 1 < end) tile(std::true_type{}, std::integral_constant<int, 1>{}, i + 1);
+    }
+  };
+  int i = t0;
+  masked_pairs(i, i_lo);
+  for (; i < i_hi; i += 2) {
+    tile(std::false_type{}, std::integral_constant<int, 0>{}, i);
+    tile(std::false_type{}, std::integral_constant<int, 1>{}, i + 1);
   }
+  masked_pairs(i, n_qt);
 
   if (kok) {
 #pragma unroll

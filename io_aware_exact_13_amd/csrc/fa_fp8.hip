@@ -379,7 +379,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
   const int kv_end = CAUSAL ? min(N, q0 + kBR) : N;
   c.n_tiles = (kv_end + kBC - 1) / kBC;
   c.kv_end = kv_end;
-  int j_mask = (N - 1) / kBC;
+  int j_mask = N / kBC;                                 // the first tile holding a key >= N
   if (CAUSAL) j_mask = min(j_mask, q0 / kBC);
   j_mask = min(j_mask, c.n_tiles);
 

@@ -751,7 +751,7 @@ void fa_fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   c.n_tiles = SPLIT ? (int)((long long)(split + 1) * all_tiles / n_ranges) : all_tiles;
   c.kv_end = min(kv_end, c.n_tiles * kBC);              // copies past it read zeros, no traffic
   // tiles from j_mask on hold keys past the end or past some query of the block
-  int j_mask = (N - 1) / kBC;                           // the tile holding key N-1
+  int j_mask = N / kBC;                                 // the first tile holding a key >= N
   if (CAUSAL) j_mask = min(j_mask, q0 / kBC);           // first tile with a key > q0
   j_mask = min(j_mask, c.n_tiles);
   const size_t prow = ((size_t)split * BH + bh) * (size_t)N;   // partial row base (SPLIT)

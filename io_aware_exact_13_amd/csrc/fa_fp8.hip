@@ -206,11 +206,13 @@ template <int D, bool MASKED>
 __device__ __forceinline__ float softmax_tile(f32x16 (&s)[2], int key0, int lim, int h, float c_log2,
                                               RowState8<D>& st, i32x8& pf, bool* rescale) {
   if (MASKED) {
+    // register r of block b holds key key0 + 32 h + (16 b + r): one compare per score
+    const int room = lim - key0 - 32 * h;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (key0 + 32 * h + 16 * b + r > lim) s[b][r] = -INFINITY;
+        if (16 * b + r > room) s[b][r] = -INFINITY;
   }
   float part[32];
 #pragma unroll

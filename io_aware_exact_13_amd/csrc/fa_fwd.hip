@@ -338,13 +338,14 @@ __device__ __forceinline__ float softmax_tile(f32x16 (&s)[kKbOf<D>], int key0, i
                                               RowState<D>& st, bf16x8 (&pf)[kBCOf<D> / 16], bool* rescale) {
   constexpr int kKb = kKbOf<D>;
   if (MASKED) {
+    // register r of block kb holds key key0 + 4 h + (32 kb + 8 (r / 4) + r % 4),
+    // visible while that offset is <= room: one compare per score
+    const int room = lim - key0 - 4 * h;
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        if (key > lim) s[kb][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + (r >> 2) * 8 + (r & 3) > room) s[kb][r] = -INFINITY;
   }
   // row max: a three-way tree over this lane's 16 kKb scores (v_max3),
   // then the other half's
@@ -434,13 +435,14 @@ __device__ __forceinline__ bool softmax_tile_lagged(f32x16 (&s)[kKbOf<D>], int k
                                                     float* lt) {
   constexpr int kKb = kKbOf<D>;
   if (MASKED) {
+    // register r of block kb holds key key0 + 4 h + (32 kb + 8 (r / 4) + r % 4),
+    // visible while that offset is <= room: one compare per score
+    const int room = lim - key0 - 4 * h;
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + kb * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        if (key > lim) s[kb][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + (r >> 2) * 8 + (r & 3) > room) s[kb][r] = -INFINITY;
   }
   float sum = exp_tile<D>(s, c_log2, -m_ref, pf);
   // Materialise P and the sum here: without these empty asm uses the

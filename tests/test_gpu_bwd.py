@@ -36,6 +36,18 @@ SMALL = [
     (1, 1, 65, 128, False), (1, 1, 65, 64, True),
     (3, 1, 129, 128, True),
 ]
+# Tile-count edge cases of the gradient loops: the dK/dV kernel walks
+# 32-row query tiles and the dQ kernel 64-key tiles, interior tiles in pairs
+# and the diagonal, tail and leftover tiles masked.  One, two, three and
+# five tiles, exact multiples and ragged tails, several key blocks.
+EDGE = [
+    (1, 1, 32, 128, True), (1, 1, 32, 64, False),
+    (1, 2, 64, 128, False), (2, 1, 96, 64, True),
+    (1, 1, 160, 128, True), (1, 1, 192, 128, False),
+    (1, 2, 320, 64, True), (1, 1, 384, 128, True),
+    (2, 1, 1056, 128, True), (1, 1, 1056, 64, False),
+    (1, 1, 1000, 128, False), (1, 2, 777, 64, True),
+]
 
 
 def run_fwd_bwd(q, k, v, do, scale, causal):
@@ -58,7 +70,7 @@ def check_tensor(name, got, ref):
     assert r_max <= MAX_REL and r_mean <= MEAN_REL, name
 
 
-@pytest.mark.parametrize("B,H,N,d,causal", SMALL)
+@pytest.mark.parametrize("B,H,N,d,causal", SMALL + EDGE)
 def test_small_shapes_match_oracle_gradients(B, H, N, d, causal):
     w = workloads.custom(B, H, N, d, causal, seed=2000 + N + d + int(causal))
     q, k, v = workloads.make_inputs(w)

@@ -43,6 +43,16 @@
 
 #include "fa.h"
 
+// VALU instructions of the softmax the scheduler places after each MFMA of a
+// step (the rest follow the step's last MFMA); a build may override them to
+// measure other placements
+#ifndef FA8_VALU_PER_MFMA_D128
+#define FA8_VALU_PER_MFMA_D128 16
+#endif
+#ifndef FA8_VALU_PER_MFMA_D64
+#define FA8_VALU_PER_MFMA_D64 32
+#endif
+
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -300,7 +310,7 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   // each MFMA pair: the next pair's LDS reads (4 transposed + 2 row reads),
   // two MFMAs, and a share of the softmax's VALU work after each (mask 0x008
   // MFMA, 0x100 LDS read, 0x002 VALU)
-  constexpr int kValu = D == 128 ? 16 : 32;
+  constexpr int kValu = D == 128 ? FA8_VALU_PER_MFMA_D128 : FA8_VALU_PER_MFMA_D64;
   __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
   for (int i = 0; i < kN; ++i) {

@@ -44,19 +44,22 @@
 //   * The softmax works in base 2 with scale*log2(e) folded into one FMA
 //     before v_exp_f32.  Any reference maximum gives the same acc / l, so
 //     the reference lags the true row maximum: for d = 128 it moves only
-//     when the tile's row maximum exceeds it by more than kSlack (2^8), so
-//     the accumulator rescale is skipped on most tiles.  For d = 64, where
-//     the MFMA work per tile halves and the softmax's VALU work does not,
-//     not even the row maximum is formed: P is taken against the current
-//     reference, and only if a lane's tile sum of P passes kPMax (2^32; also
-//     the first tile, where the reference is -inf) does the wave redo the
-//     tile with the true maximum.
+//     when the tile's row maximum passes it by more than a slack (at most
+//     kSlack = 2^8, and less while the new key's weight would exceed kShare
+//     of the row's sum so far), so the accumulator rescale is skipped on
+//     most tiles.  For d = 64, where the MFMA work per tile halves and the
+//     softmax's VALU work does not, the first FA_D64_MAX_TILES tiles take the
+//     row maximum and the rest do not form it: P is taken against the
+//     current reference, and only if a lane's tile sum of P passes its limit
+//     (kPMax = 2^32, or kShare of the lane's sum so far) does the wave redo
+//     the tile with the true maximum.
 //   * Workgroup order: workgroups are dealt round-robin to the 8 XCDs, each
 //     with its own L2.  The block index is remapped so that an XCD walks
 //     whole heads one after another: the workgroups running on it at any
-//     time stream the same head's K/V, which then stays in its L2 (reads past
-//     the L2 grow linearly with N).  Under the causal mask a head's longest
-//     query blocks launch first.
+//     time stream the same head's K/V through its L2.  Blocks that start
+//     after a head's first batch re-read its K/V past the L2, so those reads
+//     grow faster than N.  Under the causal mask a head's longest query
+//     blocks launch first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -61,8 +61,20 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kQBlock = kWaves * 32;   // query rows per dQ workgroup
 constexpr int kKTile = 64;             // keys per K/V tile in the dQ kernel
-constexpr int kKBlock = kWaves * 32;   // keys per dK/dV workgroup
-constexpr int kQTile = 32;             // query rows per Q/dO tile in the dK/dV kernel
+// The dK/dV kernel: FA_BWD_KV_WAVES waves of 32 keys each; 4 (two
+// workgroups per CU, 32-row query tiles, one barrier per 32 MFMAs a wave) or
+// 8 (one workgroup per CU, 64-row query tiles as two 32-row halves, one
+// barrier per 64 MFMAs).  The default is the measured choice; a build may
+// override it to measure the other.
+#ifndef FA_BWD_KV_WAVES
+#define FA_BWD_KV_WAVES 4
+#endif
+static_assert(FA_BWD_KV_WAVES == 4 || FA_BWD_KV_WAVES == 8, "waves per dK/dV workgroup");
+constexpr int kKvWaves = FA_BWD_KV_WAVES;
+constexpr int kKvThreads = kKvWaves * 64;
+constexpr int kKBlock = kKvWaves * 32;   // keys per dK/dV workgroup
+constexpr int kQTile = kKvWaves == 8 ? 64 : 32;   // query rows per Q/dO tile in the dK/dV kernel
+constexpr int kQHalves = kQTile / 32;             // 32-row halves of a tile, one after another
 
 // Workgroup -> (head, block): each XCD walks whole heads one after another,
 // so the workgroups running on it share one head's streamed tiles in its L2.
@@ -244,14 +256,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 }
 
 // ---------------------------------------------------------------- dK, dV
-// One workgroup per (head, block of 128 keys); lane l of wave w owns key
-// k0 + 32 w + l % 32.  Per 32-row query tile:
+// One workgroup per (head, block of kKBlock keys); lane l of wave w owns key
+// k0 + 32 w + l % 32.  Per query tile, for each of its 32-row halves:
 //   S  = Q K^T,  dP = dO V^T              (A: Q, dO rows from LDS; B: K rows
 //                                          from the resident LDS block, V in registers)
 //   P  = exp2(S c - LSE log2 e),  dS = P (dP - D)      (rows past N or above the key give 0)
 //   dV^T += dO^T P,  dK^T += Q^T dS       (A: dO^T, Q^T by transposed reads; B: P, dS)
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void fa_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int BH, int N, int n_kblocks, float c_log2,
@@ -259,10 +271,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   constexpr int kDs = D / 16, kCt = D / 32;
   constexpr int kTileBytes = kQTile * 2 * D;
   constexpr int kStatBytes = 512;                        // 64 LSE then 64 D floats
+  static_assert(kQTile <= 64, "one statistics copy covers 64 rows");
   constexpr int kBufBytes = 2 * kTileBytes + kStatBytes;  // Q tile, dO tile, statistics
   constexpr int kKBytes = kKBlock * 2 * D;                // the workgroup's K rows, resident
-  using Copy = TileCopy<D, kQTile, kThreads>;
-  using KCopy = TileCopy<D, kKBlock, kThreads>;
+  using Copy = TileCopy<D, kQTile, kKvThreads>;
+  using KCopy = TileCopy<D, kKBlock, kKvThreads>;
   __shared__ __attribute__((aligned(1024))) char lds[kKBytes + 2 * kBufBytes];
   char* const kblk = lds + 2 * kBufBytes;
 
@@ -325,41 +338,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     const char* dOt = Qt + kTileBytes;
     const char* St = Qt + 2 * kTileBytes;
 
-    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < kDs; ++ks) {
-      s = mfma32(row_operand<D>(Qt, 0, ks, lane), row_operand<D>(kblk, 32 * wave, ks, lane), s);
-      dp = mfma32(row_operand<D>(dOt, 0, ks, lane), vf[ks], dp);
-    }
-
-    // register r: query i 32 + (r / 4) 8 + 4 h + r % 4; its LSE and D sit
-    // four at a time in the statistics tile
-    bf16x8 pf[2], dsf[2];
-    // masked tiles: register r holds query q = i 32 + 4 h + (8 m + e); it is
-    // visible when q - key = dq + 8 m + e >= 0 and 8 m + e < N - (i 32 + 4 h)
-    const int dq = i * kQTile + 4 * h - key, rem = N - i * kQTile - 4 * h;
+    for (int hf = 0; hf < kQHalves; ++hf) {   // the tile's 32-row halves, one after another
+      // (kept apart: overlapping the halves would need both halves' S and dP
+      // in registers at once)
+      if (hf > 0) __builtin_amdgcn_sched_barrier(0);
+      const int r0 = 32 * hf;
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f32x4 lse4 = *reinterpret_cast<const f32x4*>(St + (8 * m + 4 * h) * 4);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(St + 256 + (8 * m + 4 * h) * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * m + e;
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -lse4[e] * kLog2e));
-        float p = pe;
-        if constexpr (kMasked) p = (8 * m + e < rem && (!CAUSAL || dq >= -(8 * m + e))) ? pe : 0.f;
-        pf[r >> 3][r & 7] = (__bf16)p;
-        dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[e]));
+      for (int ks = 0; ks < kDs; ++ks) {
+        s = mfma32(row_operand<D>(Qt, r0, ks, lane), row_operand<D>(kblk, 32 * wave, ks, lane), s);
+        dp = mfma32(row_operand<D>(dOt, r0, ks, lane), vf[ks], dp);
       }
-    }
+
+      // register r: query i kQTile + r0 + (r / 4) 8 + 4 h + r % 4; its LSE
+      // and D sit four at a time in the statistics tile
+      bf16x8 pf[2], dsf[2];
+      // masked tiles: register r holds query q = i kQTile + r0 + 4 h + (8 m + e);
+      // it is visible when q - key = dq + 8 m + e >= 0 and 8 m + e < N - (q - 8 m - e)
+      const int qb = i * kQTile + r0 + 4 * h;
+      const int dq = qb - key, rem = N - qb;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(St + (r0 + 8 * m + 4 * h) * 4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(St + 256 + (r0 + 8 * m + 4 * h) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * m + e;
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -lse4[e] * kLog2e));
+          float p = pe;
+          if constexpr (kMasked) p = (8 * m + e < rem && (!CAUSAL || dq >= -(8 * m + e))) ? pe : 0.f;
+          pf[r >> 3][r & 7] = (__bf16)p;
+          dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[e]));
+        }
+      }
 
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) {
-        acc_dv[ct] = mfma32(tr_operand<D>(dOt, 16 * t, ct, lane), pf[t], acc_dv[ct]);
-        acc_dk[ct] = mfma32(tr_operand<D>(Qt, 16 * t, ct, lane), dsf[t], acc_dk[ct]);
-      }
+        for (int ct = 0; ct < kCt; ++ct) {
+          acc_dv[ct] = mfma32(tr_operand<D>(dOt, r0 + 16 * t, ct, lane), pf[t], acc_dv[ct]);
+          acc_dk[ct] = mfma32(tr_operand<D>(Qt, r0 + 16 * t, ct, lane), dsf[t], acc_dk[ct]);
+        }
+    }
   };
   // Every (key, query) pair of tile i is visible to the whole workgroup
   // when its first query is at or past the block's last key and its last
@@ -408,7 +429,7 @@ void launch_bwd(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16*
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(BH * nqb)), dim3(kThreads), 0, stream,
                      q, k, v, dout, lse, delta, dq, BH, N, nqb, c_log2, scale);
   const int nkb = (N + kKBlock - 1) / kKBlock;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(BH * nkb)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(BH * nkb)), dim3(kKvThreads), 0, stream,
                      q, k, v, dout, lse, delta, dk, dv, BH, N, nkb, c_log2, scale);
 }
 

@@ -12,9 +12,10 @@
 //     dS = P (dP - D),   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
 //
 // gfx950 design (not taken from the pages):
-//   * Three launches on the caller's stream: D = rowsum(dO * O) into the
-//     caller's fp32 workspace; dQ by query blocks (K and V tiles stream
-//     through LDS); dK and dV by key blocks (Q and dO tiles stream through
+//   * Two launches on the caller's stream: dQ by query blocks (K and V
+//     tiles stream through LDS), which also forms D = rowsum(dO * O) for its
+//     rows and writes it to the caller's fp32 workspace; then dK and dV by
+//     key blocks (Q and dO tiles and those rows' LSE and D stream through
 //     LDS).  Each output is written by one workgroup: no atomics, and the
 //     result is bitwise reproducible.
 //   * All products run on v_mfma_f32_32x32x16_bf16 with the operand that a
@@ -116,38 +117,18 @@ __device__ __forceinline__ void load_row_operands(const __bf16* rowp, bool ok, i
   }
 }
 
-// ---------------------------------------------------------------- D = rowsum(dO * O)
-template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(const __bf16* __restrict__ O,
-                                                           const __bf16* __restrict__ dO,
-                                                           float* __restrict__ delta, long long rows) {
-  constexpr int kLanesPerRow = D / 8;
-  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
-  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
-  const int part = threadIdx.x % kLanesPerRow;
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(O + row * D + part * 8);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dO + row * D + part * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
-  }
-#pragma unroll
-  for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) delta[row] = acc;
-}
-
 // ---------------------------------------------------------------- dQ
 // One workgroup per (head, block of 128 query rows); lane l of wave w owns
-// query q0 + 32 w + l % 32.  Per 64-key tile:
+// query q0 + 32 w + l % 32.  First D = rowsum(dO * O) of the rows (also
+// written out for the dK/dV kernel), then per 64-key tile:
 //   S^T  = K Q^T,  dP^T = V dO^T          (A: K, V rows from LDS; B: Q, dO in registers)
 //   P    = exp2(S^T c - LSE log2 e),  dS = P (dP - D)   (masked keys give 0)
 //   dQ^T += K^T dS^T                      (A: K^T by transposed reads; B: dS from registers)
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void fa_bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    __bf16* __restrict__ dQ, int BH, int N, int n_qblocks, float c_log2, float scale) {
+    const __bf16* __restrict__ dO, const __bf16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ Delta, __bf16* __restrict__ dQ, int BH, int N, int n_qblocks, float c_log2, float scale) {
   constexpr int kDs = D / 16, kCt = D / 32, kKb = kKTile / 32;
   constexpr int kTileBytes = kKTile * 2 * D;
   using Copy = TileCopy<D, kKTile, kThreads>;
@@ -181,7 +162,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   load_row_operands<D>(Q + head_off + (size_t)(qok ? qrow : 0) * D, qok, h, qf);
   load_row_operands<D>(dO + head_off + (size_t)(qok ? qrow : 0) * D, qok, h, dof);
   const float neg_lse2 = qok ? -LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
-  const float dlt = qok ? Delta[(size_t)bh * N + qrow] : 0.f;
+  // D = rowsum(dO * O) of this lane's row: the lane holds half of the row's
+  // elements (16 ks + 8 h .. +7), the lane 32 apart the other half.  Written
+  // to the workspace for the dK/dV kernel, which runs after this one.
+  float dlt;
+  {
+    bf16x8 of[kDs];
+    load_row_operands<D>(O + head_off + (size_t)(qok ? qrow : 0) * D, qok, h, of);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kDs; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)of[ks][e], (float)dof[ks][e], part);
+    const unsigned u = __builtin_bit_cast(unsigned, part);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    dlt = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+    if (qok && h == 0) Delta[(size_t)bh * N + qrow] = dlt;
+  }
 
   f32x16 acc[kCt];
 #pragma unroll
@@ -420,14 +417,10 @@ template <int D, bool CAUSAL>
 void launch_bwd(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o, const float* lse,
                 const __bf16* dout, __bf16* dq, __bf16* dk, __bf16* dv, float* delta, int BH, int N,
                 float scale, hipStream_t stream) {
-  const long long rows = (long long)BH * N;
-  constexpr int kRowsPerDeltaBlock = 256 / (D / 8);
-  hipLaunchKernelGGL((fa_bwd_delta_kernel<D>), dim3((unsigned)((rows + kRowsPerDeltaBlock - 1) / kRowsPerDeltaBlock)),
-                     dim3(256), 0, stream, o, dout, delta, rows);
   const float c_log2 = scale * kLog2e;
   const int nqb = (N + kQBlock - 1) / kQBlock;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(BH * nqb)), dim3(kThreads), 0, stream,
-                     q, k, v, dout, lse, delta, dq, BH, N, nqb, c_log2, scale);
+                     q, k, v, dout, o, lse, delta, dq, BH, N, nqb, c_log2, scale);
   const int nkb = (N + kKBlock - 1) / kKBlock;
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(BH * nkb)), dim3(kKvThreads), 0, stream,
                      q, k, v, dout, lse, delta, dk, dv, BH, N, nkb, c_log2, scale);

@@ -195,8 +195,8 @@ int fa_fwd_fa1order(const void* q, const void* k, const void* v, void* o, float*
  *   B, H, N, d, scale, causal, stream: as for fa_fwd.
  *
  * Behaviour: the host checks of fa_fwd, extended to every pointer; outputs
- * and the workspace must not overlap the inputs or each other.  Three
- * kernels run in order on `stream` (D, then dQ, then dK and dV); the call
+ * and the workspace must not overlap the inputs or each other.  Two
+ * kernels run in order on `stream` (D and dQ, then dK and dV); the call
  * allocates nothing, does not synchronise and is bitwise reproducible run
  * to run (no atomics).
  */

@@ -549,25 +549,36 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
   __builtin_amdgcn_s_barrier();                      // ... and everyone's; j-1's reads done
   __builtin_amdgcn_sched_barrier(0);
 
+  // Read i: P V product (t, ct) with t fastest, S product (ks, kb) with ks
+  // fastest, so reads 2m and 2m + 1 accumulate into one block each.  Each
+  // accumulator still sums its k-steps in ascending order.
   bf16x8 v_op[kPV], k_op[kS];
+  auto pv_index = [](int i, int& t, int& ct) { t = i % kKs; ct = i / kKs; };
+  auto s_index = [](int i, int& ks, int& kb) { ks = i % kDs; kb = i / kDs; };
   auto fetch = [&](int i) {             // operands of P V read i and S read i
-    const int t = i / kCt, ct = i % kCt;
+    int t, ct, ks, kb;
+    pv_index(i, t, ct);
     v_op[i] = v_operand<D>(v_read, c.v_off[ct], t);
-    const int ks = i / kKb, kb = i % kKb;
+    s_index(i, ks, kb);
     k_op[i] = *reinterpret_cast<const bf16x8*>(k_read + c.k_off[ks] + kb * 32 * G::kRowBytes);
   };
   // each operand feeds one MFMA per row group
-  auto mfma = [&](int i) {
-    const int t = i / kCt, ct = i % kCt;
+  auto mfma_pv = [&](int i) {
+    int t, ct;
+    pv_index(i, t, ct);
 #pragma unroll
     for (int g = 0; g < kG; ++g)
       st[g].acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_op[i], p_in[g][t], st[g].acc[ct], 0, 0, 0);
-    const int ks = i / kKb, kb = i % kKb;
+  };
+  auto mfma_s = [&](int i) {
+    int ks, kb;
+    s_index(i, ks, kb);
 #pragma unroll
     for (int g = 0; g < kG; ++g)
       s_out[g][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_op[i], qf[g][ks], ks == 0 ? f32x16{} : s_out[g][kb],
                                                              0, 0, 0);
   };
+  static_assert(kKs % 2 == 0 && kDs % 2 == 0, "reads go in pairs that share an accumulator");
   // The copies go out between the MFMAs: a copy instruction holds up its
   // wave for tens of cycles at issue, which the MFMAs already in the pipe
   // cover.
@@ -578,13 +589,22 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
     if (q < G::kLoads) c.kcopy.issue(c.Kh, (j + 3) * kBC, c.kv_end, k_fill, c.wave, q);
     else c.vcopy.issue(c.Vh, (j + 1) * kBC, c.kv_end, v_fill, c.wave, q - G::kLoads);
   };
+  // Issue order per pair of reads: both P V products (back to back on one
+  // accumulator), then both S products (likewise).  Against alternating the
+  // two kinds read by read, the chip runs this order about 0.7% faster at the
+  // same results; the MFMA unit forwards a result to the next instruction
+  // that accumulates onto it.
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) fetch(i);
 #pragma unroll
-  for (int i = 0; i < kPV; ++i) {
+  for (int i = 0; i < kPV; i += 2) {
     if (i + kAhead < kPV) fetch(i + kAhead);
-    mfma(i);
-    if (i % kCopyEvery == 1) copy(i / kCopyEvery);
+    if (i + 1 + kAhead < kPV) fetch(i + 1 + kAhead);
+    mfma_pv(i);
+    mfma_pv(i + 1);
+    mfma_s(i);
+    mfma_s(i + 1);
+    if (i % kCopyEvery == 1 || (i + 1) % kCopyEvery == 1) copy((i + 1) / kCopyEvery);
   }
   // NOMAX (d = 64 past its first tiles): the lagged reference without a row
   // maximum (about 5% faster there; no gain for d = 128, whose MFMA work per

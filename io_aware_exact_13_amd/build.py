@@ -2,8 +2,8 @@
 
 Each source is compiled to its own object (with its own embedded gfx950 code
 object), in parallel, and the objects are linked into one shared library.
-Build variants override compile-time constants of the forward source only and
-reuse the other objects.
+A build variant overrides compile-time constants of one source (the forward
+unless VARIANT_SOURCE names another) and reuses the other objects.
 """
 from __future__ import annotations
 
@@ -58,8 +58,12 @@ TILE_VARIANTS = {
     "g2v7": ["-DFA_GROUPS_D128=2", "-DFA_VALU_PER_MFMA=7"],
     "g2nomax": ["-DFA_GROUPS_D128=2", "-DFA_NOMAX_D128=1"],
     "nomax128": ["-DFA_NOMAX_D128=1"],
+    # the gradient kernels with a wait and a workgroup barrier after every tile's LDS reads
+    "bwdracecheck": ["-DFA_BWD_EXTRA_BARRIER=1"],
 }
-TEST_VARIANTS = ("exactmax", "racecheck", "g2", "g2racecheck")
+# variants of a source other than the forward
+VARIANT_SOURCE = {"bwdracecheck": "fa_bwd.hip"}
+TEST_VARIANTS = ("exactmax", "racecheck", "g2", "g2racecheck", "bwdracecheck")
 
 
 def lib_path(variant: str | None = None) -> str:
@@ -99,22 +103,23 @@ def _link(objs, out, verbose):
 
 
 def build_all(verbose: bool = False, variants=()) -> list[str]:
-    """Compile every source (and the forward once per variant) in parallel,
-    then link the default library and one library per variant."""
+    """Compile every source (and each variant's source once more) in
+    parallel, then link the default library and one library per variant."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     jobs = [(src, _obj(name, None), []) for name, src in zip(SOURCE_NAMES, SOURCES)]
-    fwd_src = SOURCES[SOURCE_NAMES.index(FWD_SOURCE)]
-    jobs += [(fwd_src, _obj(FWD_SOURCE, v), TILE_VARIANTS[v]) for v in variants]
+    for v in variants:
+        name = VARIANT_SOURCE.get(v, FWD_SOURCE)
+        jobs.append((SOURCES[SOURCE_NAMES.index(name)], _obj(name, v), TILE_VARIANTS[v]))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with ThreadPoolExecutor(workers) as ex:
         for f in [ex.submit(_compile, s, o, e, verbose) for s, o, e in jobs]:
             f.result()
-    common = [_obj(n, None) for n in SOURCE_NAMES if n != FWD_SOURCE]
     outs = [lib_path()]
-    _link([_obj(FWD_SOURCE, None), *common], outs[0], verbose)
+    _link([_obj(n, None) for n in SOURCE_NAMES], outs[0], verbose)
     for v in variants:
+        name = VARIANT_SOURCE.get(v, FWD_SOURCE)
         outs.append(lib_path(v))
-        _link([_obj(FWD_SOURCE, v), *common], outs[-1], verbose)
+        _link([_obj(n, v if n == name else None) for n in SOURCE_NAMES], outs[-1], verbose)
     return outs
 
 

@@ -72,6 +72,19 @@ constexpr int kKTile = 64;             // keys per K/V tile in the dQ kernel
 #endif
 static_assert(FA_BWD_KV_WAVES == 4 || FA_BWD_KV_WAVES == 8, "waves per dK/dV workgroup");
 constexpr int kKvWaves = FA_BWD_KV_WAVES;
+// Race-check build (FA_BWD_EXTRA_BARRIER=1): after each tile's LDS reads,
+// wait for every memory operation and hold a workgroup barrier, so that no
+// wave can start the next tile's copy into a buffer another wave may still
+// read.  Its gradients must equal the default build's bit for bit.
+#ifndef FA_BWD_EXTRA_BARRIER
+#define FA_BWD_EXTRA_BARRIER 0
+#endif
+__device__ __forceinline__ void race_check_barrier() {
+  if constexpr (FA_BWD_EXTRA_BARRIER) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+}
 constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kKBlock = kKvWaves * 32;   // keys per dK/dV workgroup
 constexpr int kQTile = kKvWaves == 8 ? 64 : 32;   // query rows per Q/dO tile in the dK/dV kernel
@@ -230,6 +243,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
     for (int t = 0; t < kKTile / 16; ++t)
 #pragma unroll
       for (int ct = 0; ct < kCt; ++ct) acc[ct] = mfma32(tr_operand<D>(Kt, 16 * t, ct, lane), dsf[t], acc[ct]);
+    race_check_barrier();
   };
   // Tiles [0, j_hi) hold keys visible to every row of the block (at most
   // its first row and below N); they go unmasked in pairs, the first of
@@ -378,6 +392,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kWav
           acc_dk[ct] = mfma32(tr_operand<D>(Qt, r0 + 16 * t, ct, lane), dsf[t], acc_dk[ct]);
         }
     }
+    race_check_barrier();
   };
   // Every (key, query) pair of tile i is visible to the whole workgroup
   // when its first query is at or past the block's last key and its last

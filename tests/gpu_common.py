@@ -130,6 +130,35 @@ def variant_fwd(variant, q, k, v, scale, causal):
     return o, lse
 
 
+def variant_bwd(variant, q, k, v, o, lse, dout, scale, causal):
+    """fa_bwd of a variant build of the library (build.py TEST_VARIANTS),
+    loaded beside the default one through its own handle; every tensor on
+    the GPU.  Returns (dq, dk, dv) after a synchronisation."""
+    import ctypes
+    from io_aware_exact_13_amd.build import lib_path
+    key = ("bwd", variant)
+    lib = _variant_libs.get(key)
+    if lib is None:
+        path = lib_path(variant)
+        if not os.path.exists(path):
+            raise RuntimeError(f"variant library {path} is not built")
+        lib = ctypes.CDLL(path)
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        lib.fa_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
+        lib.fa_bwd.restype = ci
+        _variant_libs[key] = lib
+    B, H, N, d = q.shape
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device)
+    ptrs = [t.data_ptr() for t in (q, k, v, o, lse, dout, dq, dk, dv, delta)]
+    st = lib.fa_bwd(*ptrs, B, H, N, d, ctypes.c_float(scale), int(bool(causal)), stream.cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"{variant} fa_bwd returned {st}")
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
 def compare_rows(q, k, v, scale, causal, o, lse, picks):
     """picks: list of (b, h, rows).  Returns max|dO|, mean|dO|, max|dLSE| over them."""
     worst_o, worst_l, tot, cnt = 0.0, 0.0, 0.0, 0

@@ -19,7 +19,7 @@ import torch
 import io_aware_exact_13_amd as fa
 import oracle
 import workloads
-from gpu_common import announce, device, to64
+from gpu_common import announce, device, to64, variant_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +158,26 @@ def test_gradients_are_bitwise_deterministic():
     b = run_fwd_bwd(q, k, v, do, w.scale, True)[2:]
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,workload", [
+    (2, 3, 777, 128, True, None), (1, 3, 333, 64, False, None), (1, 2, 1000, 64, True, None),
+    (3, 1, 1025, 128, True, None), (1, 2, 4096, 128, False, None), (0, 0, 0, 0, False, "causal_b1h32_n16384_d128")])
+def test_extra_barrier_build_gradients_are_bitwise_equal(B, H, N, d, causal, workload):
+    """The gradient kernels' race-check build waits for every memory
+    operation and holds a workgroup barrier after each tile's LDS reads, so no
+    wave can refill a double buffer another wave may still read.  Its
+    gradients must equal the default build's bit for bit."""
+    dev = device()
+    w = workloads.WORKLOADS[workload] if workload else workloads.custom(B, H, N, d, causal, seed=6100 + N)
+    announce(f"[bwd racecheck] {w.name}")
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    do = workloads.make_grad(w).to(dev)
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
+    ref = fa.bwd(q, k, v, o, lse, do, scale=w.scale, causal=w.causal)
+    got = variant_bwd("bwdracecheck", q, k, v, o, lse, do, w.scale, w.causal)
+    for name, a, b in zip(("dq", "dk", "dv"), ref, got):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
 
 
 def test_long_sequence_gradients():

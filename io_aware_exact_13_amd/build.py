@@ -60,10 +60,12 @@ TILE_VARIANTS = {
     "nomax128": ["-DFA_NOMAX_D128=1"],
     # the gradient kernels with a wait and a workgroup barrier after every tile's LDS reads
     "bwdracecheck": ["-DFA_BWD_EXTRA_BARRIER=1"],
+    # the FP8 forward with a wait and a workgroup barrier after every step's LDS reads
+    "fp8racecheck": ["-DFA8_EXTRA_BARRIER=1"],
 }
 # variants of a source other than the forward
-VARIANT_SOURCE = {"bwdracecheck": "fa_bwd.hip"}
-TEST_VARIANTS = ("exactmax", "racecheck", "g2", "g2racecheck", "bwdracecheck")
+VARIANT_SOURCE = {"bwdracecheck": "fa_bwd.hip", "fp8racecheck": "fa_fp8.hip"}
+TEST_VARIANTS = ("exactmax", "racecheck", "g2", "g2racecheck", "bwdracecheck", "fp8racecheck")
 
 
 def lib_path(variant: str | None = None) -> str:

@@ -52,6 +52,13 @@
 #ifndef FA8_VALU_PER_MFMA_D64
 #define FA8_VALU_PER_MFMA_D64 32
 #endif
+// Race-check build (FA8_EXTRA_BARRIER=1): after each step's LDS reads, wait
+// for every memory operation and hold a workgroup barrier, so no wave can
+// refill a ring buffer another wave may still read.  Its results must equal
+// the default build's bit for bit.
+#ifndef FA8_EXTRA_BARRIER
+#define FA8_EXTRA_BARRIER 0
+#endif
 
 namespace {
 
@@ -319,6 +326,12 @@ __device__ __forceinline__ void step(const char* __restrict__ k_read, const char
     __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+  }
+  if constexpr (FA8_EXTRA_BARRIER) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (rescale) {
 #pragma unroll

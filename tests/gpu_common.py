@@ -159,6 +159,35 @@ def variant_bwd(variant, q, k, v, o, lse, dout, scale, causal):
     return dq, dk, dv
 
 
+def variant_fwd_fp8(variant, q8, k8, v8, qd, kd, vd, scale, causal):
+    """fa_fwd_fp8 of a variant build of the library (build.py TEST_VARIANTS),
+    loaded beside the default one through its own handle; every tensor on
+    the GPU.  Returns (o, lse) after a synchronisation."""
+    import ctypes
+    from io_aware_exact_13_amd.build import lib_path
+    key = ("fp8", variant)
+    lib = _variant_libs.get(key)
+    if lib is None:
+        path = lib_path(variant)
+        if not os.path.exists(path):
+            raise RuntimeError(f"variant library {path} is not built")
+        lib = ctypes.CDLL(path)
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        lib.fa_fwd_fp8.argtypes = [vp] * 8 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
+        lib.fa_fwd_fp8.restype = ci
+        _variant_libs[key] = lib
+    B, H, N, d = q8.shape
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    stream = torch.cuda.current_stream(q8.device)
+    ptrs = [t.data_ptr() for t in (q8, k8, v8, qd, kd, vd, o, lse)]
+    st = lib.fa_fwd_fp8(*ptrs, B, H, N, d, ctypes.c_float(scale), int(bool(causal)), stream.cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"{variant} fa_fwd_fp8 returned {st}")
+    torch.cuda.synchronize()
+    return o, lse
+
+
 def compare_rows(q, k, v, scale, causal, o, lse, picks):
     """picks: list of (b, h, rows).  Returns max|dO|, mean|dO|, max|dLSE| over them."""
     worst_o, worst_l, tot, cnt = 0.0, 0.0, 0.0, 0

@@ -252,4 +252,7 @@ def test_tile_variant_libraries_are_named_apart():
     from io_aware_exact_13_amd import build
     names = {build.lib_path()} | {build.lib_path(v) for v in build.TILE_VARIANTS}
     assert len(names) == 1 + len(build.TILE_VARIANTS)
-    assert all(flag.startswith("-DFA_") for fl in build.TILE_VARIANTS.values() for flag in fl)
+    assert all(flag.startswith(("-DFA_", "-DFA8_")) for fl in build.TILE_VARIANTS.values() for flag in fl)
+    assert set(build.VARIANT_SOURCE) <= set(build.TILE_VARIANTS)
+    assert set(build.VARIANT_SOURCE.values()) <= set(build.SOURCE_NAMES)
+    assert set(build.TEST_VARIANTS) <= set(build.TILE_VARIANTS)

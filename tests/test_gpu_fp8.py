@@ -19,7 +19,7 @@ import torch
 import io_aware_exact_13_amd as fa
 import oracle
 import workloads
-from gpu_common import announce, bf16_half_ulp, device, e4m3_p_bounds, fp8_flip_allowance, to64
+from gpu_common import announce, bf16_half_ulp, device, e4m3_p_bounds, fp8_flip_allowance, to64, variant_fwd_fp8
 from oracle import fp8 as ofp8
 
 pytestmark = pytest.mark.gpu
@@ -278,6 +278,27 @@ def test_fp8_special_cases():
     o, lse = gpu_fwd_fp8(qq, kk, vv, w.scale, False)
     mean_v = ofp8.dequantize_heads(*vv)[0, 0].mean(axis=0)
     assert np.all(np.abs(to64(o[0, 0]) - mean_v) <= bf16_half_ulp(mean_v) + 1e-5)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,workload", [
+    (2, 3, 777, 128, True, None), (1, 3, 333, 64, False, None), (1, 2, 1000, 64, True, None),
+    (3, 1, 1025, 128, True, None), (0, 0, 0, 0, False, "causal_b1h32_n16384_d128")])
+def test_fp8_extra_barrier_build_is_bitwise_equal(B, H, N, d, causal, workload):
+    """The FP8 forward's race-check build waits for every memory operation
+    and holds a workgroup barrier after each step's LDS reads, so no wave can
+    refill a ring buffer another wave may still read.  Its results must
+    equal the default build's bit for bit."""
+    dev = device()
+    w = workloads.WORKLOADS[workload] if workload else workloads.custom(B, H, N, d, causal, seed=6500 + N)
+    announce(f"[fp8 racecheck] {w.name}")
+    q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
+    signs = workloads.make_fp8_signs(w.seed, w.d)
+    (q8, qd), (k8, kd), (v8, vd) = (fa.quant_fp8(x, rotate=r, sign_bits=signs if r else 0)
+                                    for x, r in ((q, True), (k, True), (v, False)))
+    o, lse = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=w.causal)
+    o2, l2 = variant_fwd_fp8("fp8racecheck", q8, k8, v8, qd, kd, vd, w.scale, w.causal)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), l2.view(torch.int32))
 
 
 def test_fp8_is_bitwise_deterministic():

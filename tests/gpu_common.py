@@ -102,10 +102,10 @@ def compare_all_heads(q, k, v, scale, causal, o, lse, workers=None):
 _variant_libs = {}
 
 
-def variant_fwd(variant, q, k, v, scale, causal):
-    """fa_fwd of a variant build of the library (build.py TEST_VARIANTS),
-    loaded beside the default one through its own handle; q, k, v on the GPU.
-    Returns (o, lse) after a synchronisation."""
+def variant_lib(variant):
+    """A variant build of the library (build.py TEST_VARIANTS), loaded beside
+    the default one through its own handle, with the argument types of the
+    entry points the tests call on it."""
     import ctypes
     from io_aware_exact_13_amd.build import lib_path
     lib = _variant_libs.get(variant)
@@ -114,77 +114,79 @@ def variant_fwd(variant, q, k, v, scale, causal):
         if not os.path.exists(path):
             raise RuntimeError(f"variant library {path} is not built")
         lib = ctypes.CDLL(path)
-        vp, ci = ctypes.c_void_p, ctypes.c_int
-        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, vp]
-        lib.fa_fwd.restype = ci
+        vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_fwd.argtypes = [vp] * 5 + [ci, ci, ci, ci, cf, ci, vp]
+        lib.fa_fwd_splitkv.argtypes = [vp] * 5 + [ci, ci, ci, ci, cf, ci, ci, vp, vp, vp]
+        lib.fa_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, cf, ci, vp]
+        lib.fa_fwd_fp8.argtypes = [vp] * 8 + [ci, ci, ci, ci, cf, ci, vp]
+        for f in (lib.fa_fwd, lib.fa_fwd_splitkv, lib.fa_bwd, lib.fa_fwd_fp8):
+            f.restype = ci
         _variant_libs[variant] = lib
+    return lib
+
+
+def _variant_call(variant, name, st):
+    if st != 0:
+        raise RuntimeError(f"{variant} {name} returned {st}")
+    torch.cuda.synchronize()
+
+
+def variant_fwd(variant, q, k, v, scale, causal):
+    """fa_fwd of a variant build; q, k, v on the GPU.  Returns (o, lse)
+    after a synchronisation."""
+    lib = variant_lib(variant)
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device)
-    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
-                    ctypes.c_float(scale), int(bool(causal)), stream.cuda_stream)
-    if st != 0:
-        raise RuntimeError(f"{variant} fa_fwd returned {st}")
-    torch.cuda.synchronize()
+    _variant_call(variant, "fa_fwd", lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                 lse.data_ptr(), B, H, N, d, scale, int(bool(causal)),
+                                                 stream.cuda_stream))
+    return o, lse
+
+
+def variant_fwd_splitkv(variant, q, k, v, scale, causal, n_splits):
+    """fa_fwd_splitkv of a variant build with its own workspaces; q, k, v on
+    the GPU.  Returns (o, lse) after a synchronisation."""
+    lib = variant_lib(variant)
+    B, H, N, d = q.shape
+    f32 = dict(dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), **f32)
+    o_part = torch.empty((n_splits, B, H, N, d), **f32)
+    lse_part = torch.empty((n_splits, B, H, N), **f32)
+    stream = torch.cuda.current_stream(q.device)
+    _variant_call(variant, "fa_fwd_splitkv",
+                  lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     B, H, N, d, scale, int(bool(causal)), n_splits, o_part.data_ptr(),
+                                     lse_part.data_ptr(), stream.cuda_stream))
     return o, lse
 
 
 def variant_bwd(variant, q, k, v, o, lse, dout, scale, causal):
-    """fa_bwd of a variant build of the library (build.py TEST_VARIANTS),
-    loaded beside the default one through its own handle; every tensor on
-    the GPU.  Returns (dq, dk, dv) after a synchronisation."""
-    import ctypes
-    from io_aware_exact_13_amd.build import lib_path
-    key = ("bwd", variant)
-    lib = _variant_libs.get(key)
-    if lib is None:
-        path = lib_path(variant)
-        if not os.path.exists(path):
-            raise RuntimeError(f"variant library {path} is not built")
-        lib = ctypes.CDLL(path)
-        vp, ci = ctypes.c_void_p, ctypes.c_int
-        lib.fa_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
-        lib.fa_bwd.restype = ci
-        _variant_libs[key] = lib
+    """fa_bwd of a variant build; every tensor on the GPU.  Returns
+    (dq, dk, dv) after a synchronisation."""
+    lib = variant_lib(variant)
     B, H, N, d = q.shape
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device)
     ptrs = [t.data_ptr() for t in (q, k, v, o, lse, dout, dq, dk, dv, delta)]
-    st = lib.fa_bwd(*ptrs, B, H, N, d, ctypes.c_float(scale), int(bool(causal)), stream.cuda_stream)
-    if st != 0:
-        raise RuntimeError(f"{variant} fa_bwd returned {st}")
-    torch.cuda.synchronize()
+    _variant_call(variant, "fa_bwd", lib.fa_bwd(*ptrs, B, H, N, d, scale, int(bool(causal)), stream.cuda_stream))
     return dq, dk, dv
 
 
 def variant_fwd_fp8(variant, q8, k8, v8, qd, kd, vd, scale, causal):
-    """fa_fwd_fp8 of a variant build of the library (build.py TEST_VARIANTS),
-    loaded beside the default one through its own handle; every tensor on
-    the GPU.  Returns (o, lse) after a synchronisation."""
-    import ctypes
-    from io_aware_exact_13_amd.build import lib_path
-    key = ("fp8", variant)
-    lib = _variant_libs.get(key)
-    if lib is None:
-        path = lib_path(variant)
-        if not os.path.exists(path):
-            raise RuntimeError(f"variant library {path} is not built")
-        lib = ctypes.CDLL(path)
-        vp, ci = ctypes.c_void_p, ctypes.c_int
-        lib.fa_fwd_fp8.argtypes = [vp] * 8 + [ci, ci, ci, ci, ctypes.c_float, ci, vp]
-        lib.fa_fwd_fp8.restype = ci
-        _variant_libs[key] = lib
+    """fa_fwd_fp8 of a variant build; every tensor on the GPU.  Returns
+    (o, lse) after a synchronisation."""
+    lib = variant_lib(variant)
     B, H, N, d = q8.shape
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     stream = torch.cuda.current_stream(q8.device)
     ptrs = [t.data_ptr() for t in (q8, k8, v8, qd, kd, vd, o, lse)]
-    st = lib.fa_fwd_fp8(*ptrs, B, H, N, d, ctypes.c_float(scale), int(bool(causal)), stream.cuda_stream)
-    if st != 0:
-        raise RuntimeError(f"{variant} fa_fwd_fp8 returned {st}")
-    torch.cuda.synchronize()
+    _variant_call(variant, "fa_fwd_fp8",
+                  lib.fa_fwd_fp8(*ptrs, B, H, N, d, scale, int(bool(causal)), stream.cuda_stream))
     return o, lse
 
 

@@ -11,7 +11,7 @@ import torch
 import io_aware_exact_13_amd as fa
 import workloads
 from gpu_common import (O_MAX_ABS, O_MEAN_ABS, LSE_MAX_ABS, announce, compare_all_heads, compare_full,
-                        compare_rows, device, run_gpu, sample_picks, to64, variant_fwd)
+                        compare_rows, device, run_gpu, sample_picks, to64, variant_fwd, variant_fwd_splitkv)
 
 pytestmark = pytest.mark.gpu
 
@@ -291,6 +291,12 @@ def test_extra_barrier_build_is_bitwise_equal(B, H, N, d, causal, workload):
     o2, l2 = variant_fwd("racecheck", q, k, v, w.scale, w.causal)
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), l2.view(torch.int32))
+    # the split-KV kernel, compiled from the same source, the same way
+    n_splits = 3
+    o3, l3 = fa.fwd_splitkv(q, k, v, scale=w.scale, causal=w.causal, n_splits=n_splits)
+    o4, l4 = variant_fwd_splitkv("racecheck", q, k, v, w.scale, w.causal, n_splits)
+    assert torch.equal(o3.view(torch.int16), o4.view(torch.int16))
+    assert torch.equal(l3.view(torch.int32), l4.view(torch.int32))
 
 
 @pytest.mark.parametrize("B,H,N,causal", [(1, 1, 65, False), (2, 3, 513, True), (1, 2, 1000, True),

@@ -124,7 +124,7 @@ def log(msg):
 
 
 def log_sclk(when):
-    """Log the GPU shader clock level the driver reports (stderr; best effort).
+    """Log the GPU shader clock level the amdgpu kernel module reports (stderr; best effort).
 
     Reads the amdgpu sysfs table (the current level carries a '*'); no other
     program is started, since a process that has touched the GPU must not

@@ -223,6 +223,50 @@ def test_fp8_headline_shape_on_sampled_rows():
         assert worst <= 0 and ratio <= 1.0 and dl <= LSE_MAX
 
 
+def test_fp8_headline_every_element_within_the_plain_bound():
+    """1 x 32 x 16384 x 128, causal, every element of every head: the GPU's
+    E4M3 codes and factors equal the oracle's for all 32 heads, and the
+    GPU's O and LSE on those codes lie within the E4M3 bound of the plain
+    definition on the dequantised operands (the check that does not depend
+    on the kernel's key blocking), with the mean square difference at most
+    the predicted one over the whole tensor.  Rows go in blocks of 256, each
+    against the keys the causal mask leaves it (the rest carry weight 0)."""
+    dev = device()
+    w = workloads.WORKLOADS[workloads.HEADLINE]
+    q, k, v = workloads.make_inputs(w)
+    signs = workloads.make_fp8_signs(w.seed, w.d)
+    q8, qd = fa.quant_fp8(q.to(dev), rotate=True, sign_bits=signs)
+    k8, kd = fa.quant_fp8(k.to(dev), rotate=True, sign_bits=signs)
+    v8, vd = fa.quant_fp8(v.to(dev), rotate=False)
+    o, lse = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    codes = [(x8.cpu().numpy(), xs.cpu().numpy()) for x8, xs in ((q8, qd), (k8, kd), (v8, vd))]
+    worst, worst_l, sq, pred = -np.inf, 0.0, 0.0, 0.0
+    for h in range(w.H):
+        qq, kk, vv = oracle_quant(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], True, signs)
+        for (c, sc), (g8, gs) in zip((qq, kk, vv), codes):
+            assert np.array_equal(g8[:, h:h + 1], c), f"codes of head {h}"
+            assert np.array_equal(gs[:, h:h + 1].view(np.uint32), sc.view(np.uint32)), f"factors of head {h}"
+        qd64, kd64, vd64 = (ofp8.dequantize_heads(c, sc)[0, 0] for c, sc in (qq, kk, vv))
+        for r0 in range(0, w.N, 256):
+            r1 = min(w.N, r0 + 256)
+            rows = np.arange(r0, r1)
+            ro, rl, bound, var = e4m3_p_bounds(qd64, kd64[:r1], vd64[:r1], w.scale, True, rows)
+            go = to64(o[0, h, r0:r1])
+            gl = to64(lse[0, h, r0:r1])
+            diff = np.abs(go - ro)
+            half = bf16_half_ulp(ro)
+            worst = max(worst, float((diff - (half + bound + 1e-5)).max()))
+            worst_l = max(worst_l, float(np.abs(gl - rl).max()))
+            sq += float((diff * diff).sum())
+            pred += float((var + half * half / 3.0).sum())
+        announce(f"[fp8-headline-all] head {h}: |dO| - bound so far {worst:.3e}, max|dLSE| {worst_l:.3e}")
+    announce(f"    all heads: |dO| - bound {worst:.3e}  mean square / predicted {sq / pred:.3f}  "
+             f"max|dLSE| {worst_l:.3e}")
+    assert worst <= 0 and sq / pred <= 1.0 and worst_l <= LSE_MAX
+
+
 @pytest.mark.parametrize("name", ["causal_peaky_b1h8_n65536_d128", "short_b16h32_n2048_d64",
                                   "mid_b4h16_n4096_d128"])
 def test_fp8_other_workloads_on_sampled_rows(name):

@@ -59,15 +59,18 @@ def run_fwd_bwd(q, k, v, do, scale, causal):
     return o, lse, dq, dk, dv
 
 
-def check_tensor(name, got, ref):
+def check_tensor(name, got, ref, quiet=False):
+    """Hold one gradient tensor to the bar; returns its two ratios."""
     diff = np.abs(got - ref)
     big = float(np.abs(ref).max())
     mean_ref = float(np.abs(ref).mean())
     r_max = float(diff.max()) / big if big > 0 else float(diff.max())
     r_mean = float(diff.mean()) / mean_ref if mean_ref > 0 else float(diff.mean())
-    announce(f"    {name}: max|diff|/max|ref|={r_max:.3e}  mean|diff|/mean|ref|={r_mean:.3e}")
+    if not quiet:
+        announce(f"    {name}: max|diff|/max|ref|={r_max:.3e}  mean|diff|/mean|ref|={r_mean:.3e}")
     assert np.isfinite(got).all(), name
     assert r_max <= MAX_REL and r_mean <= MEAN_REL, name
+    return r_max, r_mean
 
 
 def _random_shapes(seed, count):
@@ -97,9 +100,10 @@ def test_small_shapes_match_oracle_gradients(B, H, N, d, causal):
 
 
 @pytest.mark.parametrize("name", ["causal_b1h32_n16384_d128", "mid_b4h16_n4096_d128"])
-def test_full_size_gradients_on_sampled_heads(name):
-    """Full sizes; the oracle recomputes two whole heads (all rows) of dK and dV
-    and sampled rows of dQ of two more."""
+def test_full_size_gradients_every_head(name):
+    """Full sizes, every element: the oracle recomputes dQ, dK and dV of every
+    head (all rows), each held to the bar per head, and the gradients are
+    bitwise equal run to run."""
     w = workloads.WORKLOADS[name]
     announce(f"[bwd-full] {name}: generating inputs")
     q, k, v = workloads.make_inputs(w)
@@ -113,22 +117,17 @@ def test_full_size_gradients_on_sampled_heads(name):
     del again
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()
-    heads = [(0, 0), (w.B - 1, w.H - 1)]
-    for b, h in heads:
-        announce(f"[bwd-full] {name}: oracle head ({b},{h})")
-        rq, rk, rv = oracle.attention_bwd_head(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]),
-                                               w.scale, w.causal)
-        for tn, got, ref in (("dQ", dq[b, h], rq), ("dK", dk[b, h], rk), ("dV", dv[b, h], rv)):
-            check_tensor(f"{tn}[{b},{h}]", to64(got), ref)
-    rng = np.random.default_rng(11)
-    rows = sorted(set(rng.integers(0, w.N, 16).tolist()) | {0, w.N - 1})
-    for b, h in [(0, w.H // 2), (w.B // 2, 1)]:
-        ref = oracle.attention_bwd_rows(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]),
-                                        w.scale, w.causal, rows)
-        got = to64(dq[b, h])[rows]
-        err = np.abs(got - ref).max() / np.abs(ref).max()
-        announce(f"    dQ rows of head ({b},{h}): max|diff|/max|ref|={err:.3e}")
-        assert err <= MAX_REL
+    worst = {"dQ": [0.0, 0.0], "dK": [0.0, 0.0], "dV": [0.0, 0.0]}
+    for b in range(w.B):
+        for h in range(w.H):
+            rq, rk, rv = oracle.attention_bwd_head(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]),
+                                                   w.scale, w.causal)
+            for tn, got, ref in (("dQ", dq[b, h], rq), ("dK", dk[b, h], rk), ("dV", dv[b, h], rv)):
+                r = check_tensor(f"{tn}[{b},{h}]", to64(got), ref, quiet=True)
+                worst[tn] = [max(worst[tn][0], r[0]), max(worst[tn][1], r[1])]
+            announce(f"[bwd-full] {name}: head ({b},{h}) within the bar")
+    for tn, (r_max, r_mean) in worst.items():
+        announce(f"    {tn}, worst head: max|diff|/max|ref|={r_max:.3e}  mean|diff|/mean|ref|={r_mean:.3e}")
 
 
 def test_gradient_special_cases():

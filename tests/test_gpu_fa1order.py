@@ -6,7 +6,7 @@ import torch
 
 import io_aware_exact_13_amd as fa
 import workloads
-from gpu_common import O_MAX_ABS, O_MEAN_ABS, LSE_MAX_ABS, announce, compare_full, device
+from gpu_common import O_MAX_ABS, O_MEAN_ABS, LSE_MAX_ABS, announce, compare_all_heads, compare_full, device
 
 pytestmark = pytest.mark.gpu
 
@@ -44,3 +44,6 @@ def test_fa1_order_agrees_with_fa2_order_at_size():
     d_l = float((l1 - l2).abs().max())
     announce(f"[fa1order] {w.name} vs fa_fwd: max|dO|={d_o:.3e} max|dLSE|={d_l:.3e}")
     assert d_o <= O_MAX_ABS and d_l <= LSE_MAX_ABS
+    mo, me, ml, _ = compare_all_heads(*(t.cpu() for t in (q, k, v)), w.scale, w.causal, o1.cpu(), l1.cpu())
+    announce(f"    every element vs the oracle: max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS

@@ -59,6 +59,28 @@ def compare_full(q, k, v, scale, causal, o, lse, with_rounding=False):
     return do.max(), do.mean(), dl.max()
 
 
+class oracle_threads:
+    """Context for running the oracle on a thread pool: yields a worker
+    count (up to 8, half the usable cores) and limits each worker's BLAS to
+    its share of the cores meanwhile."""
+
+    def __enter__(self):
+        try:
+            from threadpoolctl import threadpool_limits
+        except ImportError:  # pragma: no cover
+            threadpool_limits = None
+        cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+        cores = min(cores, 16)
+        workers = max(1, min(8, cores // 2))
+        self._limit = threadpool_limits(limits=max(1, cores // workers)) if threadpool_limits else None
+        return workers
+
+    def __exit__(self, *exc):
+        if self._limit is not None:
+            self._limit.restore_original_limits()
+        return False
+
+
 def compare_all_heads(q, k, v, scale, causal, o, lse, workers=None):
     """Every element of every (b, h) against the oracle, one head per task on
     a thread pool (the oracle's BLAS calls and ufuncs release the GIL).

@@ -12,6 +12,8 @@ bar per element is |dO| <= half a bf16 ulp of O + the move of one such flip
 bf16 ulp by (the error the bf16 output does not explain) <= 1e-4; and
 |dLSE| <= 1e-3 (the LSE adds unrounded P on both sides).
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -19,7 +21,8 @@ import torch
 import io_aware_exact_13_amd as fa
 import oracle
 import workloads
-from gpu_common import announce, bf16_half_ulp, device, e4m3_p_bounds, fp8_flip_allowance, to64, variant_fwd_fp8
+from gpu_common import (announce, bf16_half_ulp, device, e4m3_p_bounds, fp8_flip_allowance, oracle_threads, to64,
+                        variant_fwd_fp8)
 from oracle import fp8 as ofp8
 
 pytestmark = pytest.mark.gpu
@@ -223,45 +226,59 @@ def test_fp8_headline_shape_on_sampled_rows():
         assert worst <= 0 and ratio <= 1.0 and dl <= LSE_MAX
 
 
-def test_fp8_headline_every_element_within_the_plain_bound():
-    """1 x 32 x 16384 x 128, causal, every element of every head: the GPU's
-    E4M3 codes and factors equal the oracle's for all 32 heads, and the
-    GPU's O and LSE on those codes lie within the E4M3 bound of the plain
-    definition on the dequantised operands (the check that does not depend
-    on the kernel's key blocking), with the mean square difference at most
-    the predicted one over the whole tensor.  Rows go in blocks of 256, each
-    against the keys the causal mask leaves it (the rest carry weight 0)."""
+@pytest.mark.parametrize("name", ["causal_b1h32_n16384_d128", "mid_b4h16_n4096_d128", "short_b16h32_n2048_d64"])
+def test_fp8_full_size_every_element_within_the_plain_bound(name):
+    """Full-size workloads, every element of every head: the GPU's E4M3
+    codes and factors equal the oracle's for every head, and the GPU's O and
+    LSE on those codes lie within the E4M3 bound of the plain definition on
+    the dequantised operands (the check that does not depend on the kernel's
+    key blocking), with the mean square difference at most the predicted one
+    over the whole tensor.  Rows go in blocks of 256, each (under the causal
+    mask) against the keys the mask leaves it; the rest carry weight 0."""
     dev = device()
-    w = workloads.WORKLOADS[workloads.HEADLINE]
+    w = workloads.WORKLOADS[name]
     q, k, v = workloads.make_inputs(w)
     signs = workloads.make_fp8_signs(w.seed, w.d)
-    q8, qd = fa.quant_fp8(q.to(dev), rotate=True, sign_bits=signs)
-    k8, kd = fa.quant_fp8(k.to(dev), rotate=True, sign_bits=signs)
+    rotate = w.d == 128
+    q8, qd = fa.quant_fp8(q.to(dev), rotate=rotate, sign_bits=signs)
+    k8, kd = fa.quant_fp8(k.to(dev), rotate=rotate, sign_bits=signs)
     v8, vd = fa.quant_fp8(v.to(dev), rotate=False)
-    o, lse = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=True)
+    o, lse = fa.fwd_fp8(q8, k8, v8, qd, kd, vd, scale=w.scale, causal=w.causal)
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
     codes = [(x8.cpu().numpy(), xs.cpu().numpy()) for x8, xs in ((q8, qd), (k8, kd), (v8, vd))]
-    worst, worst_l, sq, pred = -np.inf, 0.0, 0.0, 0.0
-    for h in range(w.H):
-        qq, kk, vv = oracle_quant(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], True, signs)
-        for (c, sc), (g8, gs) in zip((qq, kk, vv), codes):
-            assert np.array_equal(g8[:, h:h + 1], c), f"codes of head {h}"
-            assert np.array_equal(gs[:, h:h + 1].view(np.uint32), sc.view(np.uint32)), f"factors of head {h}"
+
+    def head(bh):
+        """(codes equal, |dO| - bound, max |dLSE|, sum of dO^2, predicted sum) of one head."""
+        b, h = divmod(bh, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        qq, kk, vv = oracle_quant(q[sl], k[sl], v[sl], rotate, signs)
+        same = all(np.array_equal(g8[sl], c) and np.array_equal(gs[sl].view(np.uint32), sc.view(np.uint32))
+                   for (c, sc), (g8, gs) in zip((qq, kk, vv), codes))
         qd64, kd64, vd64 = (ofp8.dequantize_heads(c, sc)[0, 0] for c, sc in (qq, kk, vv))
+        hw, hl, hsq, hpred = -np.inf, 0.0, 0.0, 0.0
         for r0 in range(0, w.N, 256):
             r1 = min(w.N, r0 + 256)
-            rows = np.arange(r0, r1)
-            ro, rl, bound, var = e4m3_p_bounds(qd64, kd64[:r1], vd64[:r1], w.scale, True, rows)
-            go = to64(o[0, h, r0:r1])
-            gl = to64(lse[0, h, r0:r1])
-            diff = np.abs(go - ro)
+            kmax = r1 if w.causal else w.N
+            ro, rl, bound, var = e4m3_p_bounds(qd64, kd64[:kmax], vd64[:kmax], w.scale, w.causal,
+                                               np.arange(r0, r1))
+            diff = np.abs(to64(o[b, h, r0:r1]) - ro)
             half = bf16_half_ulp(ro)
-            worst = max(worst, float((diff - (half + bound + 1e-5)).max()))
-            worst_l = max(worst_l, float(np.abs(gl - rl).max()))
-            sq += float((diff * diff).sum())
-            pred += float((var + half * half / 3.0).sum())
-        announce(f"[fp8-headline-all] head {h}: |dO| - bound so far {worst:.3e}, max|dLSE| {worst_l:.3e}")
+            hw = max(hw, float((diff - (half + bound + 1e-5)).max()))
+            hl = max(hl, float(np.abs(to64(lse[b, h, r0:r1]) - rl).max()))
+            hsq += float((diff * diff).sum())
+            hpred += float((var + half * half / 3.0).sum())
+        return same, hw, hl, hsq, hpred
+
+    worst, worst_l, sq, pred = -np.inf, 0.0, 0.0, 0.0
+    n_heads = w.B * w.H
+    with oracle_threads() as workers, ThreadPoolExecutor(workers) as ex:
+        for bh, (same, hw, hl, hsq, hpred) in enumerate(ex.map(head, range(n_heads))):
+            assert same, f"codes or factors of head {divmod(bh, w.H)}"
+            worst, worst_l, sq, pred = max(worst, hw), max(worst_l, hl), sq + hsq, pred + hpred
+            if bh % 16 == 15 or bh == n_heads - 1:
+                announce(f"[fp8-all] {name}: {bh + 1} heads, |dO| - bound so far {worst:.3e}, "
+                         f"max|dLSE| {worst_l:.3e}")
     announce(f"    all heads: |dO| - bound {worst:.3e}  mean square / predicted {sq / pred:.3f}  "
              f"max|dLSE| {worst_l:.3e}")
     assert worst <= 0 and sq / pred <= 1.0 and worst_l <= LSE_MAX

@@ -21,12 +21,12 @@ the library's plan) instead of fa_fwd.
 --fp8 measures the FP8 forward fa_fwd_fp8 on E4M3 operands that fa_quant_fp8
 made beforehand (Q and K with the Hadamard rotation), against the FP8 dense
 MFMA peak; the quantisation pass is timed separately and reported beside it.
---bwd measures fa_bwd (dQ, dK, dV from the forward's O and LSE; the three
+--bwd measures fa_bwd (dQ, dK, dV from the forward's O and LSE; the two
 kernels of one call) instead of the forward, against 2.5x the forward FLOPs.
 --all also times every named workload, forward and backward, and a non-causal N=16384, d=128 run
 (diagnostic: separates the causal overheads) on stderr.  --shape times an
-ad-hoc shape instead of a named workload (used for the HBM-traffic linearity
-check: the same shape at N=8192 and N=16384 should read about 2x, not 4x).
+ad-hoc shape instead of a named workload (used for the growth of the HBM
+traffic with N: the same shape at N = 8192, 16384, 32768 and 65536).
 """
 from __future__ import annotations
 

@@ -24,8 +24,8 @@ and a hand-computed example.  No function here is "parity unpinned".
 """
 from .attention import (softmax_rows, online_softmax_rows, attention_head_rows,
                         attention, attention_rows, probs_head)
-from .attention_bwd import attention_bwd_head, attention_bwd, attention_bwd_rows
+from .attention_bwd import attention_bwd_head, attention_bwd, attention_bwd_rows, attention_bwd_span
 
 __all__ = ["softmax_rows", "online_softmax_rows", "attention_head_rows", "attention",
            "attention_rows", "probs_head", "attention_bwd_head", "attention_bwd",
-           "attention_bwd_rows"]
+           "attention_bwd_rows", "attention_bwd_span"]

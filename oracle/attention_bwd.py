@@ -33,18 +33,23 @@ import numpy as np
 ROW_BLOCK = 256
 
 
-def attention_bwd_head(q, k, v, do, scale, causal, row_block=ROW_BLOCK):
-    """(dQ, dK, dV) of one head: q, k, v, do are [N, d] arrays."""
+def attention_bwd_span(q, k, v, do, scale, causal, r0, r1, row_block=ROW_BLOCK):
+    """Query rows [r0, r1) of one head (q, k, v, do: [N, d] arrays): their dQ
+    rows ([r1 - r0, d]) and their shares of dK and dV, the sums over these
+    rows only ([n_keys, d], n_keys = r1 under the mask, where later keys get
+    nothing from these rows, else N).  dQ rows are independent, so spans that
+    cover every row once give the head's dQ, and their shares add up to its
+    dK and dV."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     do = np.asarray(do, np.float64)
-    n = q.shape[0]
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    for r0 in range(0, n, row_block):
-        row_ids = np.arange(r0, min(r0 + row_block, n))
+    n_span_keys = r1 if causal else k.shape[0]
+    dq = np.zeros((r1 - r0, q.shape[1]))
+    dk = np.zeros((n_span_keys, k.shape[1]))
+    dv = np.zeros((n_span_keys, v.shape[1]))
+    for b0 in range(r0, r1, row_block):
+        row_ids = np.arange(b0, min(b0 + row_block, r1))
         n_keys = int(row_ids.max()) + 1 if causal else k.shape[0]
         kk = k[:n_keys]
         s = scale * (q[row_ids] @ kk.T)
@@ -58,9 +63,15 @@ def attention_bwd_head(q, k, v, do, scale, causal, row_block=ROW_BLOCK):
         dp = do[row_ids] @ v[:n_keys].T
         d_row = (p * dp).sum(axis=1)
         ds = p * (dp - d_row[:, None])
-        dq[row_ids] = scale * (ds @ kk)
+        dq[row_ids - r0] = scale * (ds @ kk)
         dk[:n_keys] += scale * (ds.T @ q[row_ids])
     return dq, dk, dv
+
+
+def attention_bwd_head(q, k, v, do, scale, causal, row_block=ROW_BLOCK):
+    """(dQ, dK, dV) of one head: q, k, v, do are [N, d] arrays.  One span
+    holding every query row."""
+    return attention_bwd_span(q, k, v, do, scale, causal, 0, np.shape(q)[0], row_block)
 
 
 def attention_bwd(q, k, v, do, scale, causal):

@@ -59,21 +59,29 @@ def compare_full(q, k, v, scale, causal, o, lse, with_rounding=False):
     return do.max(), do.mean(), dl.max()
 
 
+def oracle_cores():
+    """Cores the oracle's thread pools may use: this process's CPU set, at
+    most 16."""
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(cores, 16))
+
+
 class oracle_threads:
-    """Context for running the oracle on a thread pool: yields a worker
-    count (up to 8, half the usable cores) and limits each worker's BLAS to
-    its share of the cores meanwhile."""
+    """Context for running the oracle on a thread pool: yields a worker count
+    (one per usable core, at most 16) and holds the BLAS library to one thread
+    meanwhile.  The pool's workers call BLAS at the same time, and OpenBLAS's
+    own thread pool must not be driven from several threads at once: with
+    four workers of two BLAS threads each, the oracle's gradient of one
+    64K-token head came out wrong by a quarter of its largest element, while
+    the same call alone, or with one BLAS thread per worker, agreed to 2e-16."""
 
     def __enter__(self):
         try:
             from threadpoolctl import threadpool_limits
         except ImportError:  # pragma: no cover
             threadpool_limits = None
-        cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-        cores = min(cores, 16)
-        workers = max(1, min(8, cores // 2))
-        self._limit = threadpool_limits(limits=max(1, cores // workers)) if threadpool_limits else None
-        return workers
+        self._limit = threadpool_limits(limits=1) if threadpool_limits else None
+        return oracle_cores()
 
     def __exit__(self, *exc):
         if self._limit is not None:
@@ -81,39 +89,56 @@ class oracle_threads:
         return False
 
 
+def row_spans(n, causal, parts, align=256):
+    """Split query rows [0, n) into at most `parts` spans of similar oracle
+    work, cut at multiples of `align`.  Under the mask a row's work grows with
+    its index (rows [0, r) cost about r^2), so the cuts sit at n sqrt(i /
+    parts) there and at n i / parts without it."""
+    cuts = {0, n}
+    for i in range(1, parts):
+        f = (i / parts) ** 0.5 if causal else i / parts
+        c = int(round(n * f / align)) * align
+        if 0 < c < n:
+            cuts.add(c)
+    b = sorted(cuts)
+    return list(zip(b[:-1], b[1:]))
+
+
+def spans_per_head(n_heads, n, workers):
+    """Spans per head so that a pool of `workers` gets about two tasks each,
+    none under 256 rows."""
+    return max(1, min(-(-2 * workers // max(1, n_heads)), n // 256))
+
+
 def compare_all_heads(q, k, v, scale, causal, o, lse, workers=None):
-    """Every element of every (b, h) against the oracle, one head per task on
-    a thread pool (the oracle's BLAS calls and ufuncs release the GIL).
+    """Every element of every (b, h) against the oracle, one span of a head's
+    query rows per task on a thread pool (the oracle's BLAS calls and ufuncs
+    release the GIL).
     q, k, v: CPU bf16 [B, H, N, d]; o (bf16), lse (fp32): the GPU results on
     the CPU.  Returns max|dO|, mean|dO| over the whole tensor, max|dLSE| and
     max(|dO| - half a bf16 ulp of the oracle's O)."""
     from concurrent.futures import ThreadPoolExecutor
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
     B, H = q.shape[:2]
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
-    cores = min(cores, 16)
-    workers = workers or max(1, min(8, cores // 2, B * H))
 
-    def head(bh):
+    N = q.shape[2]
+
+    def part(task):
+        bh, r0, r1 = task
         b, h = divmod(bh, H)
-        ro, rl = oracle.attention_head_rows(q[b, h].double().numpy(), k[b, h].double().numpy(),
-                                            v[b, h].double().numpy(), scale, causal)
-        d = np.abs(o[b, h].double().numpy() - ro)
-        dl = np.abs(lse[b, h].double().numpy() - rl)
+        kmax = r1 if causal else N
+        ro, rl = oracle.attention_head_rows(q[b, h].double().numpy(), k[b, h, :kmax].double().numpy(),
+                                            v[b, h, :kmax].double().numpy(), scale, causal,
+                                            rows=np.arange(r0, r1))
+        d = np.abs(o[b, h, r0:r1].double().numpy() - ro)
+        dl = np.abs(lse[b, h, r0:r1].double().numpy() - rl)
         return float(d.max()), float(d.sum()), d.size, float(dl.max()), float((d - bf16_half_ulp(ro)).max())
 
-    def run():
+    with oracle_threads() as cores:
+        workers = workers or cores
+        spans = row_spans(N, causal, spans_per_head(B * H, N, workers))
+        tasks = [(bh, r0, r1) for bh in range(B * H) for r0, r1 in spans]
         with ThreadPoolExecutor(workers) as ex:
-            return list(ex.map(head, range(B * H)))
-
-    if threadpool_limits is not None:
-        with threadpool_limits(limits=max(1, cores // workers)):
-            res = run()
-    else:
-        res = run()
+            res = list(ex.map(part, tasks))
     mo = max(r[0] for r in res)
     me = sum(r[1] for r in res) / sum(r[2] for r in res)
     ml = max(r[3] for r in res)

@@ -21,7 +21,7 @@ import torch
 import io_aware_exact_13_amd as fa
 import oracle
 import workloads
-from gpu_common import announce, device, oracle_threads, to64, variant_bwd
+from gpu_common import announce, device, oracle_threads, row_spans, spans_per_head, to64, variant_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -101,7 +101,8 @@ def test_small_shapes_match_oracle_gradients(B, H, N, d, causal):
         check_tensor(name, to64(got), ref)
 
 
-@pytest.mark.parametrize("name", ["causal_b1h32_n16384_d128", "mid_b4h16_n4096_d128", "short_b16h32_n2048_d64"])
+@pytest.mark.parametrize("name", ["causal_b1h32_n16384_d128", "mid_b4h16_n4096_d128", "short_b16h32_n2048_d64",
+                                  "causal_peaky_b1h8_n65536_d128"])
 def test_full_size_gradients_every_head(name):
     """Full sizes, every element: the oracle recomputes dQ, dK and dV of every
     head (all rows), each held to the bar per head, and the gradients are
@@ -121,21 +122,41 @@ def test_full_size_gradients_every_head(name):
         assert torch.isfinite(t).all()
     dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
 
-    def head(bh):
+    def part(bh, r0, r1):
         b, h = divmod(bh, w.H)
-        rq, rk, rv = oracle.attention_bwd_head(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]),
-                                               w.scale, w.causal)
-        return {tn: check_tensor(f"{tn}[{b},{h}]", to64(got), ref, quiet=True)
-                for tn, got, ref in (("dQ", dq[b, h], rq), ("dK", dk[b, h], rk), ("dV", dv[b, h], rv))}
+        return oracle.attention_bwd_span(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]), w.scale,
+                                         w.causal, r0, r1)
 
     worst = {"dQ": [0.0, 0.0], "dK": [0.0, 0.0], "dV": [0.0, 0.0]}
     n_heads = w.B * w.H
-    with oracle_threads() as workers, ThreadPoolExecutor(workers) as ex:
-        for bh, r in enumerate(ex.map(head, range(n_heads))):
-            for tn, (r_max, r_mean) in r.items():
+
+    def check_heads(futures, spans):
+        for bh in range(n_heads):
+            b, h = divmod(bh, w.H)
+            rq, rk, rv = (np.zeros((w.N, w.d)) for _ in range(3))
+            for (r0, r1), f in zip(spans, futures[bh]):
+                sq, sk, sv = f.result()
+                rq[r0:r1] = sq
+                rk[:sk.shape[0]] += sk
+                rv[:sv.shape[0]] += sv
+            futures[bh] = None
+            for tn, got, ref in (("dQ", dq[b, h], rq), ("dK", dk[b, h], rk), ("dV", dv[b, h], rv)):
+                r_max, r_mean = check_tensor(f"{tn}[{b},{h}]", to64(got), ref, quiet=True)
                 worst[tn] = [max(worst[tn][0], r_max), max(worst[tn][1], r_mean)]
             if bh % 16 == 15 or bh == n_heads - 1:
                 announce(f"[bwd-full] {name}: {bh + 1} heads within the bar")
+
+    with oracle_threads() as workers, ThreadPoolExecutor(workers) as ex:
+        # each head's query rows in spans of similar work, one task each; a
+        # head's dQ is its spans' rows, its dK and dV the sums of their shares
+        spans = row_spans(w.N, w.causal, spans_per_head(n_heads, w.N, workers))
+        futures = [[ex.submit(part, bh, r0, r1) for r0, r1 in spans] for bh in range(n_heads)]
+        try:
+            check_heads(futures, spans)
+        finally:
+            for fs in futures:
+                for f in fs or ():
+                    f.cancel()
     for tn, (r_max, r_mean) in worst.items():
         announce(f"    {tn}, worst head: max|diff|/max|ref|={r_max:.3e}  mean|diff|/mean|ref|={r_mean:.3e}")
 

@@ -21,8 +21,8 @@ import torch
 import io_aware_exact_13_amd as fa
 import oracle
 import workloads
-from gpu_common import (announce, bf16_half_ulp, device, e4m3_p_bounds, fp8_flip_allowance, oracle_threads, to64,
-                        variant_fwd_fp8)
+from gpu_common import (announce, bf16_half_ulp, device, e4m3_p_bounds, fp8_flip_allowance, oracle_threads, row_spans,
+                        spans_per_head, to64, variant_fwd_fp8)
 from oracle import fp8 as ofp8
 
 pytestmark = pytest.mark.gpu
@@ -226,7 +226,8 @@ def test_fp8_headline_shape_on_sampled_rows():
         assert worst <= 0 and ratio <= 1.0 and dl <= LSE_MAX
 
 
-@pytest.mark.parametrize("name", ["causal_b1h32_n16384_d128", "mid_b4h16_n4096_d128", "short_b16h32_n2048_d64"])
+@pytest.mark.parametrize("name", ["causal_b1h32_n16384_d128", "mid_b4h16_n4096_d128", "short_b16h32_n2048_d64",
+                                  "causal_peaky_b1h8_n65536_d128"])
 def test_fp8_full_size_every_element_within_the_plain_bound(name):
     """Full-size workloads, every element of every head: the GPU's E4M3
     codes and factors equal the oracle's for every head, and the GPU's O and
@@ -248,8 +249,9 @@ def test_fp8_full_size_every_element_within_the_plain_bound(name):
     o, lse = o.cpu(), lse.cpu()
     codes = [(x8.cpu().numpy(), xs.cpu().numpy()) for x8, xs in ((q8, qd), (k8, kd), (v8, vd))]
 
-    def head(bh):
-        """(codes equal, |dO| - bound, max |dLSE|, sum of dO^2, predicted sum) of one head."""
+    def part(bh, s0, s1):
+        """(codes equal, |dO| - bound, max |dLSE|, sum of dO^2, predicted sum)
+        of query rows [s0, s1) of one head."""
         b, h = divmod(bh, w.H)
         sl = (slice(b, b + 1), slice(h, h + 1))
         qq, kk, vv = oracle_quant(q[sl], k[sl], v[sl], rotate, signs)
@@ -257,8 +259,8 @@ def test_fp8_full_size_every_element_within_the_plain_bound(name):
                    for (c, sc), (g8, gs) in zip((qq, kk, vv), codes))
         qd64, kd64, vd64 = (ofp8.dequantize_heads(c, sc)[0, 0] for c, sc in (qq, kk, vv))
         hw, hl, hsq, hpred = -np.inf, 0.0, 0.0, 0.0
-        for r0 in range(0, w.N, 256):
-            r1 = min(w.N, r0 + 256)
+        for r0 in range(s0, s1, 256):
+            r1 = min(s1, r0 + 256)
             kmax = r1 if w.causal else w.N
             ro, rl, bound, var = e4m3_p_bounds(qd64, kd64[:kmax], vd64[:kmax], w.scale, w.causal,
                                                np.arange(r0, r1))
@@ -273,10 +275,12 @@ def test_fp8_full_size_every_element_within_the_plain_bound(name):
     worst, worst_l, sq, pred = -np.inf, 0.0, 0.0, 0.0
     n_heads = w.B * w.H
     with oracle_threads() as workers, ThreadPoolExecutor(workers) as ex:
-        for bh, (same, hw, hl, hsq, hpred) in enumerate(ex.map(head, range(n_heads))):
+        spans = row_spans(w.N, w.causal, spans_per_head(n_heads, w.N, workers))
+        tasks = [(bh, s0, s1) for bh in range(n_heads) for s0, s1 in spans]
+        for (bh, s0, _), (same, hw, hl, hsq, hpred) in zip(tasks, ex.map(lambda t: part(*t), tasks)):
             assert same, f"codes or factors of head {divmod(bh, w.H)}"
             worst, worst_l, sq, pred = max(worst, hw), max(worst_l, hl), sq + hsq, pred + hpred
-            if bh % 16 == 15 or bh == n_heads - 1:
+            if s0 == spans[-1][0] and (bh % 16 == 15 or bh == n_heads - 1):
                 announce(f"[fp8-all] {name}: {bh + 1} heads, |dO| - bound so far {worst:.3e}, "
                          f"max|dLSE| {worst_l:.3e}")
     announce(f"    all heads: |dO| - bound {worst:.3e}  mean square / predicted {sq / pred:.3f}  "

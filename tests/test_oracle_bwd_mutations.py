@@ -14,7 +14,7 @@ ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file
 MUTATIONS = {
     "no_softmax_jacobian_term": ("ds = p * (dp - d_row[:, None])", "ds = p * dp"),
     "row_term_from_plain_sum": ("d_row = (p * dp).sum(axis=1)", "d_row = dp.sum(axis=1)"),
-    "dq_without_scale": ("dq[row_ids] = scale * (ds @ kk)", "dq[row_ids] = (ds @ kk)"),
+    "dq_without_scale": ("dq[row_ids - r0] = scale * (ds @ kk)", "dq[row_ids - r0] = (ds @ kk)"),
     "dk_without_scale": ("dk[:n_keys] += scale * (ds.T @ q[row_ids])", "dk[:n_keys] += (ds.T @ q[row_ids])"),
     "dk_from_do": ("dk[:n_keys] += scale * (ds.T @ q[row_ids])", "dk[:n_keys] += scale * (ds.T @ do[row_ids])"),
     "dv_from_ds": ("dv[:n_keys] += p.T @ do[row_ids]", "dv[:n_keys] += ds.T @ do[row_ids]"),

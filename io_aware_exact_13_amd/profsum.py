@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output (CSV) as the short text kept with the sources.
 
 Usage (repo root):
-  python -m io_aware_exact_13_amd.profsum trace DIR --kernel fa_fwd_kernel [--flops F] [--skip-first | --skip N]
+  python -m io_aware_exact_13_amd.profsum trace DIR --kernel fa_fwd_kernel [--flops F] [--skip-first | --skip N | --last N]
   python -m io_aware_exact_13_amd.profsum counters DIR [DIR ...] --kernel fa_fwd_kernel
   python -m io_aware_exact_13_amd.profsum traffic --fetch DIR --write DIR --fetch-copy DIR --write-copy DIR
         --kernel fa_fwd_kernel --workload NAME --pass fwd --source fa_fwd.hip [--algorithmic BYTES]
@@ -71,11 +71,15 @@ def source_sha256(name: str) -> str:
 def cmd_trace(a) -> None:
     skip = max(a.skip, 1 if a.skip_first else 0)
     for k, durs in kernel_durations(a.dir, a.kernel).items():
-        n = skip if len(durs) > skip else 0
+        if a.last:
+            n = max(0, len(durs) - a.last)
+            note = f" (the last {len(durs) - n} in the figures below)"
+        else:
+            n = skip if len(durs) > skip else 0
+            note = {0: "", 1: " (first left out of the figures below)"}.get(
+                n, f" (first {n} left out of the figures below)")
         body = durs[n:]
         mean = statistics.fmean(body)
-        note = {0: "", 1: " (first left out of the figures below)"}.get(
-            n, f" (first {n} left out of the figures below)")
         print(f"{k}: {len(durs)} dispatches{note}")
         print(f"  mean {mean / 1e6:.4f} ms, median {statistics.median(body) / 1e6:.4f} ms, "
               f"min {min(body) / 1e6:.4f} ms, max {max(body) / 1e6:.4f} ms; first dispatch {durs[0] / 1e6:.4f} ms")
@@ -125,6 +129,8 @@ def main(argv=None) -> None:
     t.add_argument("--flops", type=float, default=None)
     t.add_argument("--skip-first", action="store_true", help="leave the first dispatch out")
     t.add_argument("--skip", type=int, default=0, help="leave the first N dispatches out (e.g. the warm-up calls)")
+    t.add_argument("--last", type=int, default=0,
+                   help="keep only the last N dispatches (e.g. the timed calls after a time-based warm-up)")
     c = sub.add_parser("counters")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--kernel", required=True)

@@ -21,7 +21,8 @@ import torch
 import io_aware_exact_13_amd as fa
 import oracle
 import workloads
-from gpu_common import announce, device, oracle_threads, row_spans, spans_per_head, to64, variant_bwd
+from gpu_common import (LSE_MAX_ABS, O_MAX_ABS, O_MEAN_ABS, announce, compare_full, device, oracle_threads,
+                        row_spans, spans_per_head, to64, variant_bwd)
 
 pytestmark = pytest.mark.gpu
 
@@ -222,3 +223,35 @@ def test_long_sequence_gradients():
                                            True)
     for tn, got, ref in (("dQ", dq[0, 0], rq), ("dK", dk[0, 0], rk), ("dV", dv[0, 0], rv)):
         check_tensor(tn, to64(got), ref)
+
+
+def test_many_heads_forward_and_gradients_on_sampled_heads():
+    """65536 heads of 160 rows (a ragged key tile each, causal): the largest
+    grids of the forward and both gradient kernels, and head offsets past
+    2^31 bytes into each 2.7 GB tensor.  Six heads (the first, the last and
+    four others) against the oracle on every element: dQ, dK and dV to the
+    gradients' bar; LSE and mean|dO| to the forward's bar outright, and O to
+    1e-2 beyond its own bf16 rounding, since the first rows of a causal head
+    average a few values of V, where |O| can pass 4 and half a bf16 ulp of the
+    stored O (2^-6 there) is itself more than 1e-2."""
+    w = workloads.custom(4, 16384, 160, 128, True, seed=5300)
+    assert w.B * w.H * w.N * w.d * 2 > 2 ** 31
+    announce(f"[many-heads] {w.name}: generating inputs")
+    q, k, v = workloads.make_inputs(w)
+    do = workloads.make_grad(w)
+    announce(f"[many-heads] {w.name}: running fa_fwd + fa_bwd")
+    o, lse, dq, dk, dv = run_fwd_bwd(q, k, v, do, w.scale, True)
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    rng = np.random.default_rng(5300)
+    heads = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        beyond, me, ml, mo = compare_full(q[sl], k[sl], v[sl], w.scale, True, o[sl].cpu(), lse[sl].cpu(),
+                                          with_rounding=True)
+        announce(f"    head ({b},{h}): max|dO|={mo:.3e} (beyond O's rounding {beyond:.3e}) mean|dO|={me:.3e} "
+                 f"max|dLSE|={ml:.3e}")
+        assert beyond <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+        refs = oracle.attention_bwd_head(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]), w.scale, True)
+        for tn, got, ref in zip(("dQ", "dK", "dV"), (dq[b, h], dk[b, h], dv[b, h]), refs):
+            check_tensor(f"{tn}[{b},{h}]", to64(got), ref)

@@ -193,11 +193,13 @@ def test_non_default_scale_and_large_scores():
         assert beyond <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
 
 
-@pytest.mark.parametrize("B,H,N,d,causal", [(1, 1, 262144, 128, True), (1, 2, 131072, 64, False)])
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 1, 262144, 128, True), (1, 2, 131072, 64, False),
+                                             (1, 1, 2097152, 128, True)])
 def test_long_sequences_on_sampled_rows(B, H, N, d, causal):
-    """Sequences 4x and 2x the longest workload's: 32-bit tile and row
-    arithmetic, the causal block order and the reference-maximum path over
-    thousands of key tiles.  Sampled rows against the oracle."""
+    """Sequences 4x, 2x and 32x the longest workload's (the last: 2M tokens,
+    512 MiB per tensor): 32-bit tile and row arithmetic, the causal block
+    order and the reference-maximum path over thousands of key tiles.
+    Sampled rows against the oracle."""
     w = workloads.custom(B, H, N, d, causal, seed=5000 + d)
     announce(f"[parity-long] {w.name}: generating inputs")
     q, k, v = workloads.make_inputs(w)

@@ -200,6 +200,19 @@ def _check_buffer(t, name, dtype, shape, device):
     return t
 
 
+def _launch_stream(stream, device):
+    """The stream a call runs on: torch's current stream of the tensors'
+    device unless one is given, and then it must belong to that device.  The
+    calls below also make that device current while they launch, as the C ABI
+    asks (fa_bwd_noalloc finds its workspace through the current device)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if stream.device != device:
+        raise ValueError(f"stream belongs to {stream.device}, the tensors to {device}")
+    return stream
+
+
 def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """Attention forward on torch tensors: returns (o, lse).
 
@@ -224,10 +237,10 @@ def fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_buffer(lse, "lse", torch.float32, (B, H, N), q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, H, N, d, float(scale), int(bool(causal)), stream.cuda_stream)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, float(scale), int(bool(causal)), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st)
     return out, lse
@@ -259,11 +272,11 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=No
     if delta is None:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_buffer(delta, "delta", torch.float32, (B, H, N), q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, float(scale),
-                int(bool(causal)), stream.cuda_stream)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, float(scale),
+                    int(bool(causal)), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
@@ -286,11 +299,11 @@ def bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, scale=None, causal=False, str
         scale = 1.0 / math.sqrt(d)
     for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         _check_buffer(t, name, torch.bfloat16, q.shape, q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    st = fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
-                        stream.cuda_stream)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                            stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_bwd_noalloc")
     return dq, dk, dv
@@ -325,11 +338,11 @@ def fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=None, out=None, lse=
                            torch.float32, (n_splits, B, H, N, d), q.device)
     lse_part = _check_buffer(torch.empty((n_splits, B, H, N), **f32) if lse_part is None else lse_part,
                              "lse_part", torch.float32, (n_splits, B, H, N), q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                        float(scale), int(bool(causal)), int(n_splits), o_part.data_ptr(), lse_part.data_ptr(),
-                        stream.cuda_stream)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                            float(scale), int(bool(causal)), int(n_splits), o_part.data_ptr(), lse_part.data_ptr(),
+                            stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_splitkv")
     return out, lse
@@ -356,11 +369,11 @@ def fwd_fa1order(q, k, v, scale=None, causal=False, out=None, lse=None, o_acc=No
                           (B, H, N, d), q.device)
     m = _check_buffer(torch.empty((B, H, N), **f32) if m is None else m, "m", torch.float32, (B, H, N), q.device)
     l = _check_buffer(torch.empty((B, H, N), **f32) if l is None else l, "l", torch.float32, (B, H, N), q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    st = fa_fwd_fa1order(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                         float(scale), int(bool(causal)), o_acc.data_ptr(), m.data_ptr(), l.data_ptr(),
-                         stream.cuda_stream)
+    stream = _launch_stream(stream, q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_fa1order(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                             float(scale), int(bool(causal)), o_acc.data_ptr(), m.data_ptr(), l.data_ptr(),
+                             stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_fa1order")
     return out, lse
@@ -379,11 +392,11 @@ def quant_fp8(x, rotate=False, sign_bits=0, out=None, descale=None, stream=None)
     _check_buffer(out, "out", torch.uint8, x.shape, x.device)
     descale = torch.empty((B, H), dtype=torch.float32, device=x.device) if descale is None else descale
     _check_buffer(descale, "descale", torch.float32, (B, H), x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device)
+    stream = _launch_stream(stream, x.device)
     bits = int(sign_bits)
-    st = fa_quant_fp8(x.data_ptr(), out.data_ptr(), descale.data_ptr(), B, H, N, d, int(bool(rotate)),
-                      bits & 0xFFFFFFFFFFFFFFFF, (bits >> 64) & 0xFFFFFFFFFFFFFFFF, stream.cuda_stream)
+    with torch.cuda.device(x.device):
+        st = fa_quant_fp8(x.data_ptr(), out.data_ptr(), descale.data_ptr(), B, H, N, d, int(bool(rotate)),
+                          bits & 0xFFFFFFFFFFFFFFFF, (bits >> 64) & 0xFFFFFFFFFFFFFFFF, stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_quant_fp8")
     return out, descale
@@ -412,11 +425,11 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, scale=None, causal=Fals
     _check_buffer(out, "out", torch.bfloat16, q8.shape, q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
     _check_buffer(lse, "lse", torch.float32, (B, H, N), q8.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q8.device)
-    st = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
-                    v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
-                    int(bool(causal)), stream.cuda_stream)
+    stream = _launch_stream(stream, q8.device)
+    with torch.cuda.device(q8.device):
+        st = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
+                        v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, float(scale),
+                        int(bool(causal)), stream.cuda_stream)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_fp8")
     return out, lse

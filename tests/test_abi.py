@@ -256,3 +256,15 @@ def test_tile_variant_libraries_are_named_apart():
     assert set(build.VARIANT_SOURCE) <= set(build.TILE_VARIANTS)
     assert set(build.VARIANT_SOURCE.values()) <= set(build.SOURCE_NAMES)
     assert set(build.TEST_VARIANTS) <= set(build.TILE_VARIANTS)
+
+
+def test_a_stream_of_another_device_is_rejected_before_any_call():
+    """The Python calls launch on the tensors' device; a given stream must
+    belong to it (host logic only: a stand-in stream object, no GPU)."""
+    import types
+    import torch
+    other = types.SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=0)
+    with pytest.raises(ValueError, match="stream belongs to cuda:1"):
+        fa._launch_stream(other, torch.device("cuda", 0))
+    same = types.SimpleNamespace(device=torch.device("cuda", 0), cuda_stream=0)
+    assert fa._launch_stream(same, torch.device("cuda", 0)) is same

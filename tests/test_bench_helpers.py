@@ -1,5 +1,8 @@
-"""Host-side helpers of bench.py (no GPU): the power-diagnostic inputs and the
-traffic figures' tie to the kernel source they were measured on."""
+"""Host-side helpers of bench.py (no GPU): the power-diagnostic inputs, the
+traffic figures' tie to the kernel source they were measured on, and the
+refusal of more than one GPU."""
+import os
+
 import torch
 
 import bench
@@ -52,3 +55,16 @@ def test_committed_traffic_records_parse():
     for fname, fields in bench.traffic_records():
         assert {"workload", "pass", "source_sha256", "read_bytes", "write_bytes"} <= set(fields), fname
         assert float(fields["read_bytes"]) > 0 and float(fields["write_bytes"]) > 0
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """bench.py covers one GPU; --gpus 2 exits non-zero before touching a GPU
+    and says why."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120, cwd=root)
+    assert res.returncode == 2
+    assert "only --gpus 1 is supported" in res.stderr
+    assert res.stdout.strip() == ""

@@ -433,3 +433,43 @@ def fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, scale=None, causal=Fals
     if st != FA_OK:
         raise FaError(st, "fa_fwd_fp8")
     return out, lse
+
+
+_attention_fn = None
+
+
+def _attention_function():
+    """The torch.autograd.Function behind attention(), made on first use (the
+    module imports torch only inside its calls)."""
+    global _attention_fn
+    if _attention_fn is None:
+        import torch
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, scale, causal):
+                o, lse = fwd(q, k, v, scale=scale, causal=causal)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.scale, ctx.causal = scale, causal
+                ctx.mark_non_differentiable(lse)
+                return o, lse
+
+            @staticmethod
+            def backward(ctx, dout, _dlse):
+                q, k, v, o, lse = ctx.saved_tensors
+                dq, dk, dv = bwd(q, k, v, o, lse, dout.contiguous(), scale=ctx.scale, causal=ctx.causal)
+                return dq, dk, dv, None, None
+
+        _attention_fn = _Attention
+    return _attention_fn
+
+
+def attention(q, k, v, scale=None, causal=False, return_lse=False):
+    """Attention with autograd: O = softmax(scale Q K^T [lower-triangular]) V
+    through fa_fwd, and on backward dQ, dK, dV through fa_bwd (the gradient of
+    O only; the logsumexp, returned with return_lse, carries none).  Same
+    tensor rules as fwd: bf16 GPU tensors [B, H, N, d], contiguous."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o, lse = _attention_function().apply(q, k, v, float(scale), bool(causal))
+    return (o, lse) if return_lse else o

@@ -255,3 +255,28 @@ def test_many_heads_forward_and_gradients_on_sampled_heads():
         refs = oracle.attention_bwd_head(to64(q[b, h]), to64(k[b, h]), to64(v[b, h]), to64(do[b, h]), w.scale, True)
         for tn, got, ref in zip(("dQ", "dK", "dV"), (dq[b, h], dk[b, h], dv[b, h]), refs):
             check_tensor(f"{tn}[{b},{h}]", to64(got), ref)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 3, 333, 128, True), (1, 2, 300, 64, False)])
+def test_autograd_attention_matches_the_direct_calls(B, H, N, d, causal):
+    """fa.attention under autograd gives fa_fwd's O and, on backward, fa_bwd's
+    gradients bit for bit, also when the upstream gradient reaches it as a
+    non-contiguous view (the loss taken through a transpose)."""
+    dev = device()
+    w = workloads.custom(B, H, N, d, causal, seed=9100 + N)
+    base = [t.to(dev) for t in workloads.make_inputs(w)]
+    do = workloads.make_grad(w).to(dev)
+    ro, rl = fa.fwd(*base, scale=w.scale, causal=causal)
+    ref = fa.bwd(*base, ro, rl, do, scale=w.scale, causal=causal)
+    for through_transpose in (False, True):
+        q, k, v = (t.clone().requires_grad_() for t in base)
+        o = fa.attention(q, k, v, causal=causal)
+        if through_transpose:
+            loss = (o.transpose(1, 2).float() * do.transpose(1, 2).float()).sum()
+        else:
+            loss = (o.float() * do.float()).sum()
+        loss.backward()
+        torch.cuda.synchronize()
+        assert torch.equal(o.detach().view(torch.int16), ro.view(torch.int16))
+        for name, got, want in zip(("dq", "dk", "dv"), (q.grad, k.grad, v.grad), ref):
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (name, through_transpose)

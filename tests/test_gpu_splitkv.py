@@ -70,6 +70,26 @@ def test_one_gpu_share_of_the_16k_causal_workload():
     assert d_o <= O_MAX_ABS and d_l <= LSE_MAX_ABS
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 1, 65536, 128, True), (1, 1, 32768, 64, False)])
+def test_one_long_head_every_element(B, H, N, d, causal):
+    """The case split-KV is for: one head, a long sequence, far fewer query
+    blocks than CUs.  At the planned split count, every element against the
+    oracle and the bitwise run-to-run check."""
+    dev = device()
+    w = workloads.custom(B, H, N, d, causal, seed=3300 + d)
+    q, k, v = workloads.make_inputs(w)
+    n = fa.fa_fwd_splitkv_plan(B, H, N, d, int(causal))[0]
+    announce(f"[splitkv-long] {w.name} n_splits={n}")
+    assert n > 1
+    o, lse = run_split(q, k, v, w.scale, causal, n)
+    o2, lse2 = run_split(q, k, v, w.scale, causal, n)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+    mo, me, ml, _ = compare_all_heads(q, k, v, w.scale, causal, o.cpu(), lse.cpu())
+    announce(f"    every element: max|dO|={mo:.3e} mean|dO|={me:.3e} max|dLSE|={ml:.3e}")
+    assert mo <= O_MAX_ABS and me <= O_MEAN_ABS and ml <= LSE_MAX_ABS
+    del dev
+
+
 def test_splitkv_is_bitwise_deterministic():
     w = workloads.custom(1, 2, 900, 128, True, seed=91)
     q, k, v = workloads.make_inputs(w)
